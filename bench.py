@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Benchmark of one decode step of the FP8 paged decode-attention path on one
+MI355X, on the 64 sequences x 8192-token workload (64 query / 8 kv heads,
+head dim 128, pages of 16 tokens, FP8 e4m3 cache with per-head scales and 6 of
+128 K channels per kv head scaled by 20, split-K chunks of 512 tokens).
+
+A step = kv_write_fp8 of every sequence's newest token + validate_page_tags
++ paged_decode_attn (split-K partials + combine), all on one stream with the
+inputs resident in HBM. The same step is timed with a BF16 cache built from
+the same bf16 inputs, for the FP8/BF16 ratio.
+
+Prints one JSON line. `value` is algorithmic KV bytes per step / step time
+(GB/s). `roofline` rates the attention call (partial + combine kernels),
+timed with HIP events on the launch stream. `cpu_baseline` times the oracle
+on a bounded sample of the same workload on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("decode-attn KV GB/s (% HBM peak) + seq-steps/s, FP8 vs BF16 KV, 64×8k ctx")
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD specification
+WORKLOAD_ID = 3
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def time_steps(db, steps, warmup, torch):
+    """Warm up, then time `steps` full steps; per-call HIP events on the
+    current stream give the time of each call."""
+    for _ in range(warmup):
+        db.step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        e = ev[i]
+        e[0].record()
+        db.write_step()
+        e[1].record()
+        db.validate()
+        e[2].record()
+        db.attend()
+        e[3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kvw = [e[0].elapsed_time(e[1]) for e in ev]
+    val = [e[1].elapsed_time(e[2]) for e in ev]
+    att = [e[2].elapsed_time(e[3]) for e in ev]
+    step = [e[0].elapsed_time(e[3]) for e in ev]
+    mean = lambda xs: sum(xs) / len(xs)
+    return dict(wall_ms_per_step=wall * 1e3 / steps, step_ms=mean(step), kv_write_ms=mean(kvw),
+                validate_ms=mean(val), attn_ms=mean(att),
+                attn_ms_min=min(att), attn_ms_max=max(att))
+
+
+def cpu_baseline(batch, data, host_scales, target_s=12.0):
+    """The oracle (fp64, plain loops, all host threads) running the same
+    step on whole sequences of the workload: kv write of the newest token,
+    tag validation, attention for every query head."""
+    import numpy as np
+
+    import oracle
+    import synth
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_helpers import oracle_subset
+
+    cfg = batch.cfg
+    nthreads = os.cpu_count() or 1
+
+    def run(seqs, sub):
+        t0 = time.perf_counter()
+        for i, s in enumerate(seqs):
+            l = int(batch.seq_lens[s])
+            k, v = data[s]
+            slot = sub["bt"][i, (l - 1) // cfg.page_size] * cfg.page_size + (l - 1) % cfg.page_size
+            oracle.kv_write_fp8(k[l - 1:l], v[l - 1:l], np.array([slot], np.int64),
+                                cfg.page_size, sub["P"], synth.SCALE_PER_HEAD,
+                                host_scales[0], host_scales[1], None, sub["kc"], sub["vc"])
+        tags = np.zeros(sub["P"], np.uint32)
+        ver = oracle.validate_page_tags(tags, sub["bt"], np.zeros(sub["bt"].shape, np.uint32),
+                                        sub["lens"], cfg.page_size)
+        oracle.paged_decode_attn(
+            sub["q"], sub["kc"], sub["vc"], host_scales[0], host_scales[1], sub["bt"],
+            sub["lens"], num_kv_heads=cfg.num_kv_heads, head_dim_v=cfg.head_dim_v,
+            page_size=cfg.page_size, num_pages=sub["P"], kv_dtype=1, scale_mode=1,
+            v_in_k=False, sm_scale=cfg.sm_scale, verdict=ver, num_threads=nthreads)
+        return time.perf_counter() - t0
+
+    seqs = list(range(8))
+    sub = oracle_subset(batch, data, seqs, synth.KV_FP8, host_scales)
+    t1 = run(seqs, sub)
+    reps = int(max(1, min(100, round(target_s / max(t1, 1e-3)))))
+    t = sum(run(seqs, sub) for _ in range(reps))
+    n = len(seqs) * reps
+    kvb = n * int(batch.seq_lens[0]) * cfg.num_kv_heads * (cfg.head_dim_qk + cfg.head_dim_v)
+    return {"value": kvb / t / 1e9, "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+            "seq_steps_per_s": n / t,
+            "sample": f"{len(seqs)} whole sequences of the 64 x 8192 workload (all 64 query "
+                      f"heads), {reps} steps: kv write of the newest token, tag check, fp64 "
+                      f"attention; {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import decode_attention_fp8_write_amd as pda
+    from decode_attention_fp8_write_amd import workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pda.load()
+    batch = synth.make_batch(WORKLOAD_ID)
+    cfg = batch.cfg
+    log("generating inputs")
+    data = synth.map_seqs(lambda s: batch.kv(s), list(range(batch.B)), min(16, os.cpu_count() or 1))
+    log("building FP8 cache")
+    fp8 = workload.build(batch, pda.KV_FP8_E4M3, data=data)
+    fp8.alloc_workspace()
+    log("timing FP8 steps")
+    r8 = time_steps(fp8, args.steps, args.warmup, torch)
+    kv8 = workload.kv_bytes(batch, pda.KV_FP8_E4M3)
+    B = batch.B
+    res_bf16 = None
+    if not args.no_bf16:
+        log("building BF16 cache")
+        bf = workload.build(batch, pda.KV_BF16, data=data)
+        bf.alloc_workspace()
+        log("timing BF16 steps")
+        r16 = time_steps(bf, args.steps, args.warmup, torch)
+        kv16 = workload.kv_bytes(batch, pda.KV_BF16)
+        res_bf16 = {
+            "kv_GBps_step": kv16 / (r16["step_ms"] * 1e-3) / 1e9,
+            "kv_GBps_attn": kv16 / (r16["attn_ms"] * 1e-3) / 1e9,
+            "seq_steps_per_s": B / (r16["step_ms"] * 1e-3),
+            "step_ms": r16["step_ms"], "attn_ms": r16["attn_ms"],
+            "validate_ms": r16["validate_ms"], "kv_write_ms": r16["kv_write_ms"]}
+        del bf
+        torch.cuda.empty_cache()
+
+    step_s = r8["step_ms"] * 1e-3
+    attn_s = r8["attn_ms"] * 1e-3
+    # algorithmic bytes of one attention call: KV, q, out, block-table entries
+    q_bytes = B * cfg.num_q_heads * cfg.head_dim_qk * 2
+    out_bytes = B * cfg.num_q_heads * cfg.head_dim_v * 4
+    bt_bytes = int(np.sum(-(-batch.seq_lens // cfg.page_size))) * 4
+    attn_bytes = kv8 + q_bytes + out_bytes + bt_bytes
+    achieved = attn_bytes / attn_s / 1e9
+    seq_steps = B / step_s
+    line = {
+        "metric": METRIC,
+        "value": kv8 / step_s / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r8["step_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 KV, bf16/f16 dot2 operands, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": "64 seqs x 8192 ctx, 64 q / 8 kv heads, d128, page 16, "
+                               "FP8 e4m3 KV (per-head scales; K 6/128 channels x20), "
+                               "split-K 512; step = kv write of 64 new tokens + tag "
+                               "validation + attention",
+                   "global_batch": B, "seq_len": int(batch.seq_lens[0]),
+                   "parallelism": "single GPU"},
+        "pct_hbm_peak_step": 100.0 * kv8 / step_s / 1e9 / HBM_PEAK_GBPS,
+        "seq_steps_per_s": seq_steps,
+        "tokens_per_s": seq_steps,
+        "attn_ms": r8["attn_ms"],
+        "validate_ms": r8["validate_ms"],
+        "kv_write_ms": r8["kv_write_ms"],
+        "validate_frac_of_step": r8["validate_ms"] / r8["step_ms"],
+        "kv_GBps_attn": kv8 / attn_s / 1e9,
+        "wall_ms_per_step": r8["wall_ms_per_step"],
+        "roofline": {"kernel": "paged_decode_attn (attn_partial + attn_combine)",
+                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "algorithmic_bytes_per_launch": attn_bytes, "traffic": None},
+    }
+    if res_bf16 is not None:
+        line["bf16"] = res_bf16
+        line["fp8_over_bf16_seq_steps"] = seq_steps / res_bf16["seq_steps_per_s"]
+        line["fp8_over_bf16_attn"] = res_bf16["attn_ms"] / r8["attn_ms"]
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        line["cpu_baseline"] = cpu_baseline(batch, data, fp8.host_scales)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,763 @@
+// decode_attn.hip — single-query-per-sequence attention over a paged KV
+// cache, FP8 e4m3 or BF16, for GQA groups below 16 query rows per kv head.
+//
+// The pages describe the FP8 cache and its cost: the attention kernel has to
+// convert every cached value it reads, which made it a few percent slower
+// than BF16 at equal concurrency, while halving the memory per token
+// (aifeed.sk, "Cloudflare zrýchľuje inferenciu modelov Kimi a GLM kompresiou
+// cache a váh", section "Dve odlišné úzke miesta v pamäti GPU"; manulx.blog,
+// "Công thức của Cloudflare để phục vụ Kimi và GLM", section "Bộ nhớ đệm KV
+// FP8 tăng gấp đôi dung lượng ngữ cảnh"). The kernel design below is not from
+// the pages, which give none.
+//
+// Work decomposition. A sequence's context is cut into page-aligned chunks
+// (split-K). A work item is (sequence, chunk, kv head) and belongs to one
+// wavefront. Each workgroup first derives the item list from seq_lens and the
+// verdicts (aborted sequences get no items, so none of their pages is read),
+// then its waves take items round-robin. Partials (unnormalised output rows,
+// running max, running sum) go to the workspace; the combine kernel merges
+// them with a log-sum-exp rule.
+//
+// Inside an item a wave walks 64 tokens at a time (four 16-token lane groups):
+//  * QK: lane = token. The lane loads its token's 128 K codes (16-byte
+//    column groups of the K format, contiguous across the 16 lanes of a
+//    group), converts pairs of codes to bf16 exactly, and accumulates
+//    q·k for all G query rows with v_dot2c_f32_bf16 whose q operand is a
+//    wave-uniform value held in SGPRs.
+//  * softmax: scores in log2 units; wave max per row through DPP; the
+//    running max is only moved when the block max exceeds it by more than
+//    TAU (then p <= 2^TAU), so rescaling the accumulators is rare.
+//  * PV: lane = (16-token group, 8 dims). V pairs of adjacent tokens are
+//    interleaved in the V format, so one converted dword is an f16 pair along
+//    the token axis; p pairs are packed once per block and broadcast inside
+//    the 16-lane group with DPP row_newbcast; v_dot2c_f32_f16 accumulates
+//    G x 8 outputs per lane. BF16 caches use bf16 dots with p split into a
+//    bf16 high part and a bf16 remainder (relative error 2^-16).
+// Every dot accumulates in fp32; q enters exactly (bf16), K and V codes
+// convert exactly, and p is rounded once (f16 nearest-even, or hi+lo bf16).
+#include <mutex>
+
+#include "pda_internal.h"
+
+namespace pda {
+namespace {
+
+constexpr int kD = 128;          // head dim (qk and v) of this path
+constexpr int kThreads = 256;    // 4 waves per workgroup
+constexpr int kWaves = kThreads / 64;
+constexpr float kTau = 8.0f;     // lazy-rescale threshold, log2 units
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kHdrInts = 64;     // workspace header, then prefix[B+1]
+
+struct AttnArgs {
+  const uint16_t* __restrict__ q;
+  const uint8_t* __restrict__ kc;
+  const uint8_t* __restrict__ vc;
+  const float* __restrict__ k_scale;
+  const float* __restrict__ v_scale;
+  const int32_t* __restrict__ bt;
+  const int32_t* __restrict__ lens;
+  const int32_t* __restrict__ verdict;
+  int32_t* ws_hdr;      // [0] chunk tokens, [1] seq-chunks, then prefix[B+1]
+  float* ws_part;       // items * G * (D + 2)
+  float* out;
+  int B, Hq, Hkv, P, max_blocks;
+  int chunk0;           // requested chunk (tokens), multiple of 64 and S
+  long long cap_items;  // partials that fit in the workspace
+  float sm_scale;
+};
+
+template <int F, int L>
+struct static_for {
+  template <typename Fn>
+  __device__ __forceinline__ static void run(Fn&& fn) {
+    if constexpr (F < L) {
+      fn(std::integral_constant<int, F>{});
+      static_for<F + 1, L>::run(fn);
+    }
+  }
+};
+
+__device__ __forceinline__ int n_chunks_of(const AttnArgs& a, int s, int S, int chunk) {
+  const int len = a.lens[s];
+  if (len <= 0 || len > a.max_blocks * S) return 0;
+  if (a.verdict != nullptr && a.verdict[s] != 0) return 0;
+  return (len + chunk - 1) / chunk;
+}
+
+// Every workgroup derives the same plan: chunk size (doubled until the
+// partials fit the workspace) and the exclusive prefix of chunks per
+// sequence, kept in LDS (pref[0..B]). Workgroup 0 also publishes it.
+__device__ int build_plan(const AttnArgs& a, int S, int* pref, int* tmp, int& chunk_out) {
+  const int tid = threadIdx.x;
+  const int per = (a.B + kThreads - 1) / kThreads;
+  const int beg = min(a.B, tid * per);
+  const int end = min(a.B, beg + per);
+  int chunk = a.chunk0;
+  int total = 0;
+  for (;;) {
+    int local = 0;
+    for (int s = beg; s < end; ++s) local += n_chunks_of(a, s, S, chunk);
+    tmp[tid] = local;
+    __syncthreads();
+    if (tid == 0) {
+      int run = 0;
+      for (int i = 0; i < kThreads; ++i) {
+        const int v = tmp[i];
+        tmp[i] = run;
+        run += v;
+      }
+      tmp[kThreads] = run;
+    }
+    __syncthreads();
+    int run = tmp[tid];
+    for (int s = beg; s < end; ++s) {
+      pref[s] = run;
+      run += n_chunks_of(a, s, S, chunk);
+    }
+    total = tmp[kThreads];
+    __syncthreads();
+    if ((long long)total * a.Hkv <= a.cap_items) break;
+    chunk *= 2;
+  }
+  if (tid == 0) pref[a.B] = total;
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int s = tid; s <= a.B; s += kThreads) a.ws_hdr[kHdrInts + s] = pref[s];
+    if (tid == 0) {
+      a.ws_hdr[0] = chunk;
+      a.ws_hdr[1] = total;
+    }
+  }
+  chunk_out = chunk;
+  return total;
+}
+
+// Query rows are read through the constant address space, so uniform loads
+// become scalar loads into SGPRs. The 512 q dwords of a G = 8 group cannot
+// stay resident in SGPRs, so they are re-read every block in small chunks.
+typedef const uint32_t __attribute__((address_space(4))) cu32_t;
+
+// Opaque identity on the q pointer that also "uses and redefines" the score
+// accumulators: loads through the returned pointer cannot move above the dot
+// products that produced z, and those dot products cannot sink below it.
+template <int R>
+__device__ __forceinline__ cu32_t* fence_ptr_after(cu32_t* p, float (&z)[R]) {
+  uint64_t v = (uint64_t)(uintptr_t)p;
+  if constexpr (R == 2) {
+    asm volatile("" : "+s"(v), "+v"(z[0]), "+v"(z[1]));
+  } else if constexpr (R == 4) {
+    asm volatile("" : "+s"(v), "+v"(z[0]), "+v"(z[1]), "+v"(z[2]), "+v"(z[3]));
+  } else {
+    asm volatile("" : "+s"(v), "+v"(z[0]), "+v"(z[1]), "+v"(z[2]), "+v"(z[3]), "+v"(z[4]),
+                 "+v"(z[5]), "+v"(z[6]), "+v"(z[7]));
+  }
+  return (cu32_t*)(uintptr_t)v;
+}
+
+template <int G, bool FP8, int S>
+struct ItemCtx {
+  static constexpr int R = G < 2 ? 2 : G;     // rows carried (padded to 2)
+  static constexpr int KQ = FP8 ? 8 : 16;     // uint4 of K per lane per block
+  static constexpr int VQ = FP8 ? 8 : 16;     // uint4 of V per lane per block
+  static constexpr int E = FP8 ? 1 : 2;       // bytes per element
+};
+
+template <int G, bool FP8, int S>
+__device__ __forceinline__ void load_k(const AttnArgs& a, int g, int page, int off,
+                                       uint4 (&kk)[ItemCtx<G, FP8, S>::KQ]) {
+  using C = ItemCtx<G, FP8, S>;
+  // element (page, g, off, 16c + i) at (((page*Hkv + g)*8 + c)*S + off)*16 + i
+  const uint8_t* base = a.kc + ((((int64_t)page * a.Hkv + g) * 8) * S + off) * 16 * C::E;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    if constexpr (FP8) {
+      kk[c] = *reinterpret_cast<const uint4*>(base + (int64_t)c * S * 16);
+    } else {
+      kk[2 * c] = *reinterpret_cast<const uint4*>(base + (int64_t)c * S * 32);
+      kk[2 * c + 1] = *reinterpret_cast<const uint4*>(base + (int64_t)c * S * 32 + 16);
+    }
+  }
+}
+
+template <int G, bool FP8, int S>
+__device__ __forceinline__ void load_v(const AttnArgs& a, int g, int page, int off0, int tt,
+                                       uint4 (&vv)[ItemCtx<G, FP8, S>::VQ]) {
+  using C = ItemCtx<G, FP8, S>;
+  // element (page, g, off, d) at
+  //   (page*Hkv + g)*S*128 + ((off/2)*16 + d/8)*16 + (d%8)*2 + off%2
+  const uint8_t* base = a.vc + (((int64_t)page * a.Hkv + g) * S * kD +
+                                ((int64_t)(off0 / 2) * 16 + tt) * 16) * C::E;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if constexpr (FP8) {
+      vv[i] = *reinterpret_cast<const uint4*>(base + i * 256);
+    } else {
+      vv[2 * i] = *reinterpret_cast<const uint4*>(base + i * 512);
+      vv[2 * i + 1] = *reinterpret_cast<const uint4*>(base + i * 512 + 16);
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t u4_get(const uint4& v, int j) {
+  return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
+template <int G, bool FP8, int S>
+__device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, long long item) {
+  using C = ItemCtx<G, FP8, S>;
+  constexpr int R = C::R;
+  const int lane = __lane_id();
+  const int tg = lane >> 4;
+  const int tt = lane & 15;
+  const int len = a.lens[s];
+  const int tok0 = c * chunk;
+  const int tok1 = min(len, tok0 + chunk);
+  const int32_t* btrow = a.bt + (int64_t)s * a.max_blocks;
+  cu32_t* qbase =
+      (cu32_t*)(uintptr_t)(a.q + ((int64_t)s * a.Hq + (int64_t)g * G) * kD);
+  const float kmul = a.sm_scale * (FP8 ? a.k_scale[g] : 1.0f) * kLog2e;
+  // v_perm selector building the p pair of this lane (see pack below)
+  const uint32_t sel_f16 = (tt & 1) ? 0x03020706u : 0x05040100u;
+
+  float m[R], l[R], acc[R][8];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[r][j] = 0.0f;
+  }
+  bool bad = false;
+
+  // Physical page of this lane's 16-token group in the block starting at b0.
+  // Groups past the end of the chunk read the chunk's first page instead (a
+  // page of this sequence); their tokens are masked out below. A page id
+  // outside [0, P) is never dereferenced: it marks the item bad.
+  int fb = btrow[tok0 / S];
+  if (fb < 0 || fb >= a.P) {
+    bad = true;
+    fb = 0;
+  }
+  auto page_of = [&](int b0) -> int {
+    const int gtok = b0 + 16 * tg;
+    int p = fb;
+    if (gtok < tok1) {
+      p = btrow[gtok / S];
+      if (p < 0 || p >= a.P) {
+        bad = true;
+        p = fb;
+      }
+    }
+    return p;
+  };
+
+  uint4 kk[C::KQ];
+  uint4 vv[C::VQ];
+  int b0 = tok0;
+  {
+    const int page = page_of(b0);
+    load_k<G, FP8, S>(a, g, page, (b0 + 16 * tg) % S + tt, kk);
+    load_v<G, FP8, S>(a, g, page, (b0 + 16 * tg) % S, tt, vv);
+  }
+
+  for (;;) {
+    const int bn = b0 + 64;
+    const bool has_next = bn < tok1;
+    int npage = 0;
+    if (has_next) npage = page_of(bn);
+
+    // ---- QK: lane = token b0 + lane ------------------------------------
+    // Eight dims (four q pairs per row) at a time, q in SGPRs. The loads of
+    // chunk c+2 are released by a fence that consumes the scores produced by
+    // chunk c, so exactly two 4-pair chunks of q are live at any time.
+    const bool tok_ok = (b0 + lane) < tok1;
+    float z[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) z[r] = 0.0f;
+    {
+      uint32_t qbuf[2][G][4];
+      auto loadq = [&](int cc8, uint32_t(&dst)[G][4]) {
+        cu32_t* qp = fence_ptr_after<R>(qbase, z);
+#pragma unroll
+        for (int r = 0; r < G; ++r)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dst[r][j] = qp[r * 64 + cc8 * 4 + j];
+      };
+      loadq(0, qbuf[0]);
+      loadq(1, qbuf[1]);
+      static_for<0, 16>::run([&](auto CC) {
+        constexpr int cc8 = decltype(CC)::value;
+        bf16x2_t kp[4];
+        if constexpr (FP8) {
+          const uint32_t c0 = u4_get(kk[cc8 >> 1], (cc8 & 1) * 2);
+          const uint32_t c1 = u4_get(kk[cc8 >> 1], (cc8 & 1) * 2 + 1);
+          kp[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, 1.0f, false);
+          kp[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, 1.0f, true);
+          kp[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, 1.0f, false);
+          kp[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, 1.0f, true);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) kp[j] = __builtin_bit_cast(bf16x2_t, u4_get(kk[cc8], j));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < G; ++r)
+            z[r] = __builtin_amdgcn_fdot2_f32_bf16(
+                __builtin_bit_cast(bf16x2_t, qbuf[cc8 & 1][r][j]), kp[j], z[r], false);
+        if constexpr (cc8 + 2 < 16) loadq(cc8 + 2, qbuf[cc8 & 1]);
+      });
+    }
+    // K registers are free: prefetch the next block's keys.
+    if (has_next)
+      load_k<G, FP8, S>(a, g, npage, (bn + 16 * tg) % S + tt, kk);
+
+    // ---- online softmax ------------------------------------------------
+    float zl[R], p[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) zl[r] = (tok_ok && r < G) ? z[r] * kmul : -INFINITY;
+    bool need = false;
+    float bm[R];
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      bm[r] = wave_max(zl[r]);
+      need |= bm[r] > m[r] + kTau;
+    }
+    if (need) {
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        if (bm[r] > m[r] + kTau) {
+          const float alpha = exp2f(m[r] - bm[r]);
+          m[r] = bm[r];
+          l[r] *= alpha;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[r][j] *= alpha;
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      p[r] = (r < G) ? exp2f(zl[r] - m[r]) : 0.0f;
+      l[r] += p[r];
+    }
+
+    // ---- pack p pairs along tokens --------------------------------------
+    // Lane tt holds p of token tt for every row. Even lanes build
+    // (p[r][tt], p[r][tt+1]) for rows r < R/2, odd lanes build
+    // (p[r][tt-1], p[r][tt]) for rows r >= R/2.
+    constexpr int H = R / 2;
+    uint32_t pp[H], pplo[H];
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      if constexpr (FP8) {
+        const f16x2_t hv = {(_Float16)p[j], (_Float16)p[j + H]};
+        const uint32_t mine = __builtin_bit_cast(uint32_t, hv);
+        const uint32_t nb = dpp_u32<DPP_QUAD_1032>(mine);
+        pp[j] = __builtin_amdgcn_perm(nb, mine, sel_f16);
+      } else {
+        // hi = bf16 truncation of p, lo = bf16 truncation of the remainder
+        const uint32_t b0u = as_u32(p[j]), b1u = as_u32(p[j + H]);
+        const float r0 = p[j] - as_f32(b0u & 0xFFFF0000u);
+        const float r1 = p[j + H] - as_f32(b1u & 0xFFFF0000u);
+        const uint32_t mine_hi = __builtin_amdgcn_perm(b1u, b0u, 0x07060302u);
+        const uint32_t mine_lo = __builtin_amdgcn_perm(as_u32(r1), as_u32(r0), 0x07060302u);
+        const uint32_t nb_hi = dpp_u32<DPP_QUAD_1032>(mine_hi);
+        const uint32_t nb_lo = dpp_u32<DPP_QUAD_1032>(mine_lo);
+        pp[j] = __builtin_amdgcn_perm(nb_hi, mine_hi, sel_f16);
+        pplo[j] = __builtin_amdgcn_perm(nb_lo, mine_lo, sel_f16);
+      }
+    }
+
+    // ---- PV: lane = (token group tg, dims 8tt..8tt+7) --------------------
+    if (!(b0 + 64 <= tok1)) {
+      // tail block: zero V codes of tokens at or beyond tok1
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int t0 = b0 + 16 * tg + 2 * i;
+        const bool v0 = t0 < tok1, v1 = t0 + 1 < tok1;
+        const uint32_t msk = FP8 ? ((v0 ? 0x00FF00FFu : 0u) | (v1 ? 0xFF00FF00u : 0u))
+                                 : ((v0 ? 0x0000FFFFu : 0u) | (v1 ? 0xFFFF0000u : 0u));
+        if constexpr (FP8) {
+          vv[i].x &= msk; vv[i].y &= msk; vv[i].z &= msk; vv[i].w &= msk;
+        } else {
+          vv[2 * i].x &= msk; vv[2 * i].y &= msk; vv[2 * i].z &= msk; vv[2 * i].w &= msk;
+          vv[2 * i + 1].x &= msk; vv[2 * i + 1].y &= msk;
+          vv[2 * i + 1].z &= msk; vv[2 * i + 1].w &= msk;
+        }
+      }
+    }
+    static_for<0, 8>::run([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      uint32_t pb[R], pbl[R];
+#pragma unroll
+      for (int r = 0; r < H; ++r) {
+        pb[r] = dpp_u32<DPP_ROW_NEWBCAST0 + 2 * i>(pp[r]);
+        pb[r + H] = dpp_u32<DPP_ROW_NEWBCAST0 + 2 * i + 1>(pp[r]);
+        if constexpr (!FP8) {
+          pbl[r] = dpp_u32<DPP_ROW_NEWBCAST0 + 2 * i>(pplo[r]);
+          pbl[r + H] = dpp_u32<DPP_ROW_NEWBCAST0 + 2 * i + 1>(pplo[r]);
+        }
+      }
+      if constexpr (FP8) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t code4 = u4_get(vv[i], w);
+          const f16x2_t va = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code4, 1.0f, false);
+          const f16x2_t vb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code4, 1.0f, true);
+#pragma unroll
+          for (int r = 0; r < G; ++r) {
+            const f16x2_t ph = __builtin_bit_cast(f16x2_t, pb[r]);
+            acc[r][2 * w] = __builtin_amdgcn_fdot2(ph, va, acc[r][2 * w], false);
+            acc[r][2 * w + 1] = __builtin_amdgcn_fdot2(ph, vb, acc[r][2 * w + 1], false);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd) {
+          const bf16x2_t vp = __builtin_bit_cast(bf16x2_t, u4_get(vv[2 * i + (jd >> 2)], jd & 3));
+#pragma unroll
+          for (int r = 0; r < G; ++r) {
+            acc[r][jd] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pb[r]), vp,
+                                                         acc[r][jd], false);
+            acc[r][jd] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pbl[r]), vp,
+                                                         acc[r][jd], false);
+          }
+        }
+      }
+    });
+    if (!has_next) break;
+    load_v<G, FP8, S>(a, g, npage, (bn + 16 * tg) % S, tt, vv);
+    b0 = bn;
+  }
+
+  // ---- write the partial ------------------------------------------------
+  float* part = a.ws_part + item * (int64_t)(G * (kD + 2));
+  const bool item_bad = __ballot(bad) != 0;
+  if (item_bad) {
+    if (lane < G) part[G * kD + lane] = __builtin_nanf("");
+    return;
+  }
+  float ltot[G];
+#pragma unroll
+  for (int r = 0; r < G; ++r) ltot[r] = wave_sum(l[r]);
+#pragma unroll
+  for (int r = 0; r < G; ++r) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float x = acc[r][j];
+      x += shfl_xor_f32(x, 16);
+      x += shfl_xor_f32(x, 32);
+      acc[r][j] = x;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < G; ++r) {
+    if ((r & 3) == tg) {
+      float4* dst = reinterpret_cast<float4*>(part + r * kD + 8 * tt);
+      dst[0] = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
+      dst[1] = make_float4(acc[r][4], acc[r][5], acc[r][6], acc[r][7]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < G; ++r) {
+    if (lane == r) {
+      part[G * kD + r] = m[r];
+      part[G * kD + G + r] = ltot[r];
+    }
+  }
+}
+
+template <int G, bool FP8, int S>
+__global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a) {
+  extern __shared__ int lds[];
+  int* tmp = lds;                    // kThreads + 1
+  int* pref = lds + kThreads + 1;    // B + 1
+  int chunk;
+  const int total_sc = build_plan(a, S, pref, tmp, chunk);
+  const long long total_items = (long long)total_sc * a.Hkv;
+  const int wave = threadIdx.x >> 6;
+  const long long nw = (long long)gridDim.x * kWaves;
+  for (long long item = (long long)blockIdx.x * kWaves + wave; item < total_items; item += nw) {
+    const int sc = (int)(item / a.Hkv);
+    const int g = (int)(item % a.Hkv);
+    // sequence owning seq-chunk sc: last s with pref[s] <= sc
+    int lo = 0, hi = a.B;  // invariant pref[lo] <= sc < pref[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pref[mid] <= sc) lo = mid; else hi = mid;
+    }
+    const int s = __builtin_amdgcn_readfirstlane(lo);
+    const int c = __builtin_amdgcn_readfirstlane(sc - pref[lo]);
+    process_item<G, FP8, S>(a, s, c, __builtin_amdgcn_readfirstlane(g), chunk, item);
+  }
+}
+
+// Merge the chunk partials of one (sequence, kv head): G rows x 128 dims,
+// four dims per thread.
+template <int G, bool FP8>
+__global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a, int S) {
+  const int s = blockIdx.x / a.Hkv;
+  const int g = blockIdx.x % a.Hkv;
+  const int r = threadIdx.x >> 5;
+  const int d4 = (threadIdx.x & 31) * 4;
+  if (r >= G) return;
+  float* o = a.out + (((int64_t)s * a.Hq + (int64_t)g * G + r) * kD + d4);
+  const int len = a.lens[s];
+  const bool aborted = a.verdict != nullptr && a.verdict[s] != 0;
+  if (aborted || len == 0) {
+    *reinterpret_cast<float4*>(o) = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  const float qnan = __builtin_nanf("");
+  if (len < 0 || len > a.max_blocks * S) {
+    *reinterpret_cast<float4*>(o) = make_float4(qnan, qnan, qnan, qnan);
+    return;
+  }
+  const int* pref = a.ws_hdr + kHdrInts;
+  const int c0 = pref[s], c1 = pref[s + 1];
+  const int64_t stride = G * (kD + 2);
+  float M = -INFINITY;
+  bool nan = false;
+  for (int c = c0; c < c1; ++c) {
+    const float mc = a.ws_part[((int64_t)c * a.Hkv + g) * stride + G * kD + r];
+    nan |= __builtin_isnan(mc);
+    M = fmaxf(M, mc);
+  }
+  if (nan) {
+    *reinterpret_cast<float4*>(o) = make_float4(qnan, qnan, qnan, qnan);
+    return;
+  }
+  float L = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c = c0; c < c1; ++c) {
+    const float* pc = a.ws_part + ((int64_t)c * a.Hkv + g) * stride;
+    const float w = exp2f(pc[G * kD + r] - M);
+    L += w * pc[G * kD + G + r];
+    const float4 v = *reinterpret_cast<const float4*>(pc + r * kD + d4);
+    acc.x += w * v.x;
+    acc.y += w * v.y;
+    acc.z += w * v.z;
+    acc.w += w * v.w;
+  }
+  const float f = (FP8 ? a.v_scale[g] : 1.0f) / L;
+  *reinterpret_cast<float4*>(o) = make_float4(acc.x * f, acc.y * f, acc.z * f, acc.w * f);
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+int resolve_chunk(const pda_attn_shape& sh, int32_t max_seq_len) {
+  const int align = sh.page_size > 64 ? sh.page_size : 64;
+  if (sh.split_tokens > 0) return sh.split_tokens;
+  // automatic: 512 tokens, halved while the grid would hold fewer than
+  // 4096 items, never below one 64-token block / one page
+  int chunk = 512 < align ? align : 512;
+  const long long ml = max_seq_len > 0 ? max_seq_len : 1;
+  while (chunk > align &&
+         (long long)sh.num_seqs * sh.num_kv_heads * ((ml + chunk - 1) / chunk) < 4096)
+    chunk /= 2;
+  return chunk;
+}
+
+size_t header_bytes(int B) {
+  const size_t h = (size_t)(kHdrInts + B + 1) * sizeof(int32_t);
+  return (h + 255) & ~(size_t)255;
+}
+
+size_t item_bytes(const pda_attn_shape& sh) {
+  const int G = sh.num_q_heads / sh.num_kv_heads;
+  return (size_t)G * (sh.head_dim_v + 2) * sizeof(float);
+}
+
+// Shape checks shared by the workspace query and the call.
+int check_shape(const pda_attn_shape* sh) {
+  if (!sh) return PDA_ERR_INVALID_ARG;
+  if (sh->num_seqs < 0 || sh->num_q_heads <= 0 || sh->num_kv_heads <= 0 ||
+      sh->head_dim_qk <= 0 || sh->head_dim_v <= 0 || sh->page_size <= 0 ||
+      sh->num_pages <= 0 || sh->max_blocks_per_seq <= 0)
+    return PDA_ERR_INVALID_ARG;
+  if (sh->num_q_heads % sh->num_kv_heads != 0) return PDA_ERR_INVALID_ARG;
+  if (!(sh->sm_scale == sh->sm_scale)) return PDA_ERR_INVALID_ARG;
+  if (sh->kv_dtype != PDA_KV_BF16 && sh->kv_dtype != PDA_KV_FP8_E4M3) return PDA_ERR_INVALID_ARG;
+  if (sh->split_tokens < 0) return PDA_ERR_INVALID_ARG;
+  const int align = sh->page_size > 64 ? sh->page_size : 64;
+  if (sh->split_tokens > 0 && (sh->split_tokens % align != 0)) return PDA_ERR_INVALID_ARG;
+  if ((long long)sh->max_blocks_per_seq * sh->page_size > (1LL << 30)) return PDA_ERR_UNSUPPORTED;
+  if (sh->num_seqs > 16384) return PDA_ERR_UNSUPPORTED;
+  return PDA_OK;
+}
+
+bool valu_supported(const pda_attn_shape& sh) {
+  const int G = sh.num_q_heads / sh.num_kv_heads;
+  if (sh.v_in_k) return false;
+  if (sh.head_dim_qk != kD || sh.head_dim_v != kD) return false;
+  if (!(G == 1 || G == 2 || G == 4 || G == 8)) return false;
+  if (!(sh.page_size == 16 || sh.page_size == 32 || sh.page_size == 64)) return false;
+  if (sh.kv_dtype == PDA_KV_FP8_E4M3) return sh.scale_mode == PDA_SCALE_PER_HEAD;
+  return sh.scale_mode == PDA_SCALE_NONE;
+}
+
+typedef void (*kernel_t)(AttnArgs);
+typedef void (*combine_t)(AttnArgs, int);
+
+template <int G, bool FP8>
+kernel_t pick_partial_s(int S) {
+  switch (S) {
+    case 16: return attn_partial_kernel<G, FP8, 16>;
+    case 32: return attn_partial_kernel<G, FP8, 32>;
+    default: return attn_partial_kernel<G, FP8, 64>;
+  }
+}
+template <bool FP8>
+kernel_t pick_partial(int G, int S) {
+  switch (G) {
+    case 1: return pick_partial_s<1, FP8>(S);
+    case 2: return pick_partial_s<2, FP8>(S);
+    case 4: return pick_partial_s<4, FP8>(S);
+    default: return pick_partial_s<8, FP8>(S);
+  }
+}
+template <bool FP8>
+combine_t pick_combine(int G) {
+  switch (G) {
+    case 1: return attn_combine_kernel<1, FP8>;
+    case 2: return attn_combine_kernel<2, FP8>;
+    case 4: return attn_combine_kernel<4, FP8>;
+    default: return attn_combine_kernel<8, FP8>;
+  }
+}
+
+// Resident workgroups per CU for a partial kernel (cached per kernel).
+int blocks_per_cu(kernel_t k, size_t lds) {
+  static std::mutex mu;
+  static kernel_t keys[64];
+  static int vals[64];
+  static int n = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < n; ++i)
+    if (keys[i] == k) return vals[i];
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(k),
+                                                   kThreads, lds) != hipSuccess ||
+      nb <= 0)
+    nb = 1;
+  if (n < 64) {
+    keys[n] = k;
+    vals[n] = nb;
+    ++n;
+  }
+  return nb;
+}
+
+}  // namespace
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == 0) {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cu <= 0)
+      cu = 256;
+    cached[dev] = cu;
+  }
+  return cached[dev];
+}
+
+// Latent (MFMA) path, decode_attn_latent.hip.
+bool latent_supported(const pda_attn_shape& sh);
+size_t latent_workspace_bytes(const pda_attn_shape& sh, int32_t max_seq_len);
+int latent_launch(const pda_attn_shape& sh, const void* q, const void* k_cache,
+                  const float* token_scale, const int32_t* block_table, const int32_t* seq_lens,
+                  int32_t max_seq_len, const int32_t* verdict, void* workspace,
+                  size_t workspace_bytes, float* out, hipStream_t stream);
+
+}  // namespace pda
+
+using namespace pda;
+
+extern "C" size_t paged_decode_attn_workspace_bytes(const pda_attn_shape* shape,
+                                                    int32_t max_seq_len) {
+  if (check_shape(shape) != PDA_OK) return 0;
+  if (max_seq_len < 0) return 0;
+  const pda_attn_shape& sh = *shape;
+  if (latent_supported(sh)) return latent_workspace_bytes(sh, max_seq_len);
+  const int chunk = resolve_chunk(sh, max_seq_len);
+  const long long ml = max_seq_len > 0 ? max_seq_len : 1;
+  const long long per_seq = (ml + chunk - 1) / chunk;
+  const long long items = (long long)sh.num_seqs * per_seq * sh.num_kv_heads;
+  return header_bytes(sh.num_seqs) + (size_t)items * item_bytes(sh);
+}
+
+extern "C" int paged_decode_attn(const pda_attn_shape* shape, const void* q, const void* k_cache,
+                                 const void* v_cache, const float* k_scale,
+                                 const float* v_scale, const int32_t* block_table,
+                                 const int32_t* seq_lens, int32_t max_seq_len,
+                                 const int32_t* verdict, void* workspace,
+                                 size_t workspace_bytes, float* out, void* stream) {
+  int st = check_shape(shape);
+  if (st != PDA_OK) return st;
+  const pda_attn_shape& sh = *shape;
+  if (max_seq_len < 0) return PDA_ERR_INVALID_ARG;
+  if (sh.num_seqs == 0) return PDA_OK;
+  if (!q || !k_cache || !block_table || !seq_lens || !out || !workspace)
+    return PDA_ERR_INVALID_ARG;
+  if (latent_supported(sh)) {
+    if (v_cache || !k_scale || v_scale) return PDA_ERR_INVALID_ARG;
+    return latent_launch(sh, q, k_cache, k_scale, block_table, seq_lens, max_seq_len, verdict,
+                         workspace, workspace_bytes, out, as_stream(stream));
+  }
+  if (!valu_supported(sh)) return PDA_ERR_UNSUPPORTED;
+  if (!v_cache) return PDA_ERR_INVALID_ARG;
+  const bool fp8 = sh.kv_dtype == PDA_KV_FP8_E4M3;
+  if (fp8 && (!k_scale || !v_scale)) return PDA_ERR_INVALID_ARG;
+  if (!fp8 && (k_scale || v_scale)) return PDA_ERR_INVALID_ARG;
+  const size_t hdr = header_bytes(sh.num_seqs);
+  const size_t ib = item_bytes(sh);
+  if (workspace_bytes < hdr + (size_t)sh.num_seqs * sh.num_kv_heads * ib) return PDA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return PDA_ERR_INVALID_ARG;
+  const int G = sh.num_q_heads / sh.num_kv_heads;
+  const int chunk = resolve_chunk(sh, max_seq_len);
+
+  AttnArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kc = static_cast<const uint8_t*>(k_cache);
+  a.vc = static_cast<const uint8_t*>(v_cache);
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.bt = block_table;
+  a.lens = seq_lens;
+  a.verdict = verdict;
+  a.ws_hdr = static_cast<int32_t*>(workspace);
+  a.ws_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + hdr);
+  a.out = out;
+  a.B = sh.num_seqs;
+  a.Hq = sh.num_q_heads;
+  a.Hkv = sh.num_kv_heads;
+  a.P = sh.num_pages;
+  a.max_blocks = sh.max_blocks_per_seq;
+  a.chunk0 = chunk;
+  a.cap_items = (long long)((workspace_bytes - hdr) / ib);
+  a.sm_scale = sh.sm_scale;
+
+  const kernel_t pk = fp8 ? pick_partial<true>(G, sh.page_size) : pick_partial<false>(G, sh.page_size);
+  const combine_t ck = fp8 ? pick_combine<true>(G) : pick_combine<false>(G);
+  const size_t lds = (size_t)(kThreads + 1 + sh.num_seqs + 1) * sizeof(int);
+  const long long ml = max_seq_len > 0 ? max_seq_len : 1;
+  const long long items_bound = (long long)sh.num_seqs * sh.num_kv_heads * ((ml + chunk - 1) / chunk);
+  long long grid = (long long)device_cu_count() * blocks_per_cu(pk, lds);
+  const long long need = (items_bound + kWaves - 1) / kWaves;
+  if (grid > need) grid = need;
+  if (grid < 1) grid = 1;
+  hipStream_t s = as_stream(stream);
+  hipLaunchKernelGGL(pk, dim3((unsigned)grid), dim3(kThreads), lds, s, a);
+  if (hipGetLastError() != hipSuccess) return PDA_ERR_LAUNCH;
+  hipLaunchKernelGGL(ck, dim3((unsigned)(sh.num_seqs * sh.num_kv_heads)), dim3(kThreads), 0, s, a,
+                     (int)sh.page_size);
+  return launch_status();
+}

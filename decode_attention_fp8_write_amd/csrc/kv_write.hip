@@ -1,0 +1,221 @@
+// kv_write.hip — quantise new K/V rows to OCP FP8 e4m3 (or copy them as BF16)
+// and scatter them into their physical cache slots.
+//
+// The pages state that the KV cache is stored as 8-bit e4m3 instead of
+// 16-bit BF16, which halves its footprint (aifeed.sk, "Cloudflare zrýchľuje
+// inferenciu modelov Kimi a GLM kompresiou cache a váh", section "Dve odlišné
+// úzke miesta v pamäti GPU"; manulx.blog, "Công thức của Cloudflare để phục
+// vụ Kimi và GLM", section "Bộ nhớ đệm KV FP8 tăng gấp đôi dung lượng ngữ
+// cảnh"). Rounding, saturation and scaling are not on the pages; the reading
+// taken here (fp32 division by the scale, nearest-even, saturate to ±448,
+// keep the sign of zero, NaN -> 0x7F|sign) is stated in include/pda.h.
+//
+// One workgroup per token; each thread converts groups of 4 consecutive
+// dims, which are contiguous in the K format and two bytes apart in the V
+// format (the V format interleaves the two tokens of a slot pair).
+#include "pda_internal.h"
+
+namespace pda {
+namespace {
+
+constexpr int kThreads = 256;
+
+// e4m3 codes of four fp32 quotients packed little-endian into a dword, via
+// the gfx950 converter (OCP e4m3, round to nearest even). The converter is
+// fed values clamped to ±448 so it never sees an out-of-range magnitude:
+// every |y| >= 448 must give ±448, and clamping first is exact. NaN inputs get
+// the canonical NaN code with the input's sign.
+__device__ __forceinline__ uint32_t e4m3x4(float y0, float y1, float y2, float y3) {
+  float c0 = fminf(fmaxf(y0, -448.0f), 448.0f);
+  float c1 = fminf(fmaxf(y1, -448.0f), 448.0f);
+  float c2 = fminf(fmaxf(y2, -448.0f), 448.0f);
+  float c3 = fminf(fmaxf(y3, -448.0f), 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c2, c3, w, true);
+  uint32_t r = (uint32_t)w;
+  float ys[4] = {y0, y1, y2, y3};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (__builtin_isnan(ys[i])) {
+      uint32_t code = 0x7Fu | ((as_u32(ys[i]) >> 31) << 7);
+      r = (r & ~(0xFFu << (8 * i))) | (code << (8 * i));
+    }
+  }
+  return r;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return as_f32(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return as_f32(w & 0xFFFF0000u); }
+
+// Element index of (page, head, offset, dim) in the K format.
+__device__ __forceinline__ int64_t k_elem(int64_t page, int h, int off, int d, int hkv, int dk,
+                                          int S) {
+  return (((page * hkv + h) * (dk / 16) + d / 16) * S + off) * 16 + (d & 15);
+}
+// Element index of (page, head, offset, dim) in the V format.
+__device__ __forceinline__ int64_t v_elem(int64_t page, int h, int off, int d, int hkv, int dv,
+                                          int S) {
+  return ((((page * hkv + h) * (S / 2) + off / 2) * (dv / 8) + d / 8) * 8 + (d & 7)) * 2 +
+         (off & 1);
+}
+
+template <bool PER_TOKEN>
+__global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int64_t* __restrict__ slots, int hkv, int dk, int dv, int S, int P,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+    float* __restrict__ token_scale, uint8_t* __restrict__ k_cache,
+    uint8_t* __restrict__ v_cache) {
+  __shared__ float red[kThreads / 64];
+  const int t = blockIdx.x;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= (int64_t)P * S) return;
+  const int64_t page = slot / S;
+  const int off = (int)(slot % S);
+  const int tid = threadIdx.x;
+
+  float tok_sc = 1.0f;
+  if (PER_TOKEN) {
+    // amax over the token's K values (Hkv == 1); NaN values are ignored.
+    float amax = 0.0f;
+    const uint16_t* src = k_new + (int64_t)t * dk;
+    for (int d = tid; d < dk; d += kThreads)
+      amax = fmaxf(amax, fabsf(as_f32((uint32_t)src[d] << 16)));
+    amax = wave_max(amax);
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    tok_sc = (amax > 0.0f) ? amax / 448.0f : 1.0f;
+    if (tid == 0) token_scale[slot] = tok_sc;
+  }
+
+  // K: groups of 4 dims, contiguous in the cache.
+  const int kq = hkv * dk / 4;
+  for (int i = tid; i < kq; i += kThreads) {
+    const int h = (i * 4) / dk;
+    const int d = (i * 4) % dk;
+    const uint2 x = *reinterpret_cast<const uint2*>(k_new + ((int64_t)t * hkv + h) * dk + d);
+    const float sc = PER_TOKEN ? tok_sc : k_scale[h];
+    const uint32_t codes = e4m3x4(bf16_lo(x.x) / sc, bf16_hi(x.x) / sc, bf16_lo(x.y) / sc,
+                                  bf16_hi(x.y) / sc);
+    *reinterpret_cast<uint32_t*>(k_cache + k_elem(page, h, off, d, hkv, dk, S)) = codes;
+  }
+  if (v_new == nullptr) return;
+  // V: groups of 4 dims, two bytes apart in the cache.
+  const int vq = hkv * dv / 4;
+  for (int i = tid; i < vq; i += kThreads) {
+    const int h = (i * 4) / dv;
+    const int d = (i * 4) % dv;
+    const uint2 x = *reinterpret_cast<const uint2*>(v_new + ((int64_t)t * hkv + h) * dv + d);
+    const float sc = v_scale[h];
+    const uint32_t codes = e4m3x4(bf16_lo(x.x) / sc, bf16_hi(x.x) / sc, bf16_lo(x.y) / sc,
+                                  bf16_hi(x.y) / sc);
+    uint8_t* dst = v_cache + v_elem(page, h, off, d, hkv, dv, S);
+    dst[0] = (uint8_t)(codes);
+    dst[2] = (uint8_t)(codes >> 8);
+    dst[4] = (uint8_t)(codes >> 16);
+    dst[6] = (uint8_t)(codes >> 24);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void kv_write_bf16_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int64_t* __restrict__ slots, int hkv, int dk, int dv, int S, int P,
+    uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache) {
+  const int t = blockIdx.x;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= (int64_t)P * S) return;
+  const int64_t page = slot / S;
+  const int off = (int)(slot % S);
+  const int tid = threadIdx.x;
+  const int kq = hkv * dk / 4;
+  for (int i = tid; i < kq; i += kThreads) {
+    const int h = (i * 4) / dk;
+    const int d = (i * 4) % dk;
+    const uint2 x = *reinterpret_cast<const uint2*>(k_new + ((int64_t)t * hkv + h) * dk + d);
+    *reinterpret_cast<uint2*>(k_cache + k_elem(page, h, off, d, hkv, dk, S)) = x;
+  }
+  if (v_new == nullptr) return;
+  const int vq = hkv * dv / 4;
+  for (int i = tid; i < vq; i += kThreads) {
+    const int h = (i * 4) / dv;
+    const int d = (i * 4) % dv;
+    const uint2 x = *reinterpret_cast<const uint2*>(v_new + ((int64_t)t * hkv + h) * dv + d);
+    uint16_t* dst = v_cache + v_elem(page, h, off, d, hkv, dv, S);
+    dst[0] = (uint16_t)(x.x);
+    dst[2] = (uint16_t)(x.x >> 16);
+    dst[4] = (uint16_t)(x.y);
+    dst[6] = (uint16_t)(x.y >> 16);
+  }
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_common(const void* k_new, const void* v_new, const int64_t* slots, int32_t T,
+                 int32_t hkv, int32_t dk, int32_t dv, int32_t S, int32_t P, const void* kc,
+                 const void* vc) {
+  if (T < 0 || hkv <= 0 || dk <= 0 || S <= 0 || P <= 0) return PDA_ERR_INVALID_ARG;
+  if (T > 0 && (!k_new || !slots)) return PDA_ERR_INVALID_ARG;
+  if (!kc) return PDA_ERR_INVALID_ARG;
+  const bool latent = (v_new == nullptr);
+  if (latent != (vc == nullptr)) return PDA_ERR_INVALID_ARG;
+  if (dk % 16 != 0 || S % 2 != 0) return PDA_ERR_UNSUPPORTED;
+  if (!latent && (dv <= 0 || dv % 8 != 0)) return PDA_ERR_UNSUPPORTED;
+  if (!aligned(k_new, 8) || (!latent && !aligned(v_new, 8)) || !aligned(kc, 8))
+    return PDA_ERR_INVALID_ARG;
+  return PDA_OK;
+}
+
+}  // namespace
+}  // namespace pda
+
+using namespace pda;
+
+extern "C" int kv_write_fp8(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                            int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim_k,
+                            int32_t head_dim_v, int32_t page_size, int32_t num_pages,
+                            int32_t scale_mode, const float* k_scale, const float* v_scale,
+                            float* token_scale, uint8_t* k_cache, uint8_t* v_cache,
+                            void* stream) {
+  int st = check_common(k_new, v_new, slot_mapping, num_tokens, num_kv_heads, head_dim_k,
+                        head_dim_v, page_size, num_pages, k_cache, v_cache);
+  if (st != PDA_OK) return st;
+  const bool latent = (v_new == nullptr);
+  if (scale_mode == PDA_SCALE_PER_HEAD) {
+    if (!k_scale || (!latent && !v_scale) || token_scale) return PDA_ERR_INVALID_ARG;
+  } else if (scale_mode == PDA_SCALE_PER_TOKEN) {
+    if (!token_scale || k_scale || v_scale) return PDA_ERR_INVALID_ARG;
+    if (!latent || num_kv_heads != 1) return PDA_ERR_UNSUPPORTED;
+  } else {
+    return PDA_ERR_INVALID_ARG;
+  }
+  if (num_tokens == 0) return PDA_OK;
+  hipStream_t s = as_stream(stream);
+  const auto* kn = static_cast<const uint16_t*>(k_new);
+  const auto* vn = static_cast<const uint16_t*>(v_new);
+  if (scale_mode == PDA_SCALE_PER_TOKEN)
+    hipLaunchKernelGGL(kv_write_fp8_kernel<true>, dim3(num_tokens), dim3(kThreads), 0, s, kn,
+                       vn, slot_mapping, num_kv_heads, head_dim_k, head_dim_v, page_size,
+                       num_pages, k_scale, v_scale, token_scale, k_cache, v_cache);
+  else
+    hipLaunchKernelGGL(kv_write_fp8_kernel<false>, dim3(num_tokens), dim3(kThreads), 0, s, kn,
+                       vn, slot_mapping, num_kv_heads, head_dim_k, head_dim_v, page_size,
+                       num_pages, k_scale, v_scale, token_scale, k_cache, v_cache);
+  return launch_status();
+}
+
+extern "C" int kv_write_bf16(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                             int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim_k,
+                             int32_t head_dim_v, int32_t page_size, int32_t num_pages,
+                             void* k_cache, void* v_cache, void* stream) {
+  int st = check_common(k_new, v_new, slot_mapping, num_tokens, num_kv_heads, head_dim_k,
+                        head_dim_v, page_size, num_pages, k_cache, v_cache);
+  if (st != PDA_OK) return st;
+  if (num_tokens == 0) return PDA_OK;
+  hipLaunchKernelGGL(kv_write_bf16_kernel, dim3(num_tokens), dim3(kThreads), 0,
+                     as_stream(stream), static_cast<const uint16_t*>(k_new),
+                     static_cast<const uint16_t*>(v_new), slot_mapping, num_kv_heads, head_dim_k,
+                     head_dim_v, page_size, num_pages, static_cast<uint16_t*>(k_cache),
+                     static_cast<uint16_t*>(v_cache));
+  return launch_status();
+}

@@ -1,0 +1,13 @@
+// status.cpp — status strings of the C ABI.
+#include "pda.h"
+
+extern "C" const char* pda_status_string(int status) {
+  switch (status) {
+    case PDA_OK: return "ok";
+    case PDA_ERR_INVALID_ARG: return "invalid argument";
+    case PDA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case PDA_ERR_LAUNCH: return "kernel launch failed";
+    case PDA_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}

@@ -1,0 +1,238 @@
+"""Device-resident synthetic workloads for the benchmark and the GPU tests.
+
+Builds one decode step's inputs on the GPU from the seeded generator in
+``synth`` (input generation only) using this package's own kernels: the
+context of every sequence is written into the paged cache with
+kv_write_fp8 / kv_write_bf16, exactly as a serving step would. Nothing here
+computes attention.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+import synth
+
+from . import (KV_BF16, KV_FP8_E4M3, SCALE_NONE, SCALE_PER_HEAD, SCALE_PER_TOKEN,
+               kv_write_bf16, kv_write_fp8, make_shape, paged_decode_attn,
+               paged_decode_attn_workspace_bytes, validate_page_tags)
+
+
+def _u16(torch, a: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+
+
+@dataclass
+class DeviceBatch:
+    batch: synth.Batch
+    kv_dtype: int
+    q: object
+    k_cache: object
+    v_cache: object
+    k_scale: object          # per head [Hkv] or token scales [P*S] (latent)
+    v_scale: object
+    block_table: object
+    expected_tags: object
+    page_tags: object
+    seq_lens: object
+    verdict: object
+    out: object
+    step_k: object = None    # bf16 [B, Hkv, Dk]: the token at position len-1
+    step_v: object = None
+    step_slots: object = None
+    host_scales: tuple = field(default=(None, None))
+    workspace: object = None
+    shape: object = None
+
+    @property
+    def cfg(self):
+        return self.batch.cfg
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.batch.seq_lens.max()) if self.batch.B else 0
+
+    def make_shape(self, split_tokens: Optional[int] = None):
+        cfg = self.cfg
+        fp8 = self.kv_dtype == KV_FP8_E4M3
+        mode = (SCALE_PER_TOKEN if cfg.v_in_k else SCALE_PER_HEAD) if fp8 else SCALE_NONE
+        return make_shape(
+            num_seqs=self.batch.B, num_q_heads=cfg.num_q_heads, num_kv_heads=cfg.num_kv_heads,
+            head_dim_qk=cfg.head_dim_qk, head_dim_v=cfg.head_dim_v, page_size=cfg.page_size,
+            num_pages=self.batch.num_pages, max_blocks_per_seq=self.batch.max_blocks,
+            kv_dtype=self.kv_dtype, scale_mode=mode, v_in_k=cfg.v_in_k,
+            split_tokens=cfg.split_tokens if split_tokens is None else split_tokens,
+            sm_scale=cfg.sm_scale)
+
+    def alloc_workspace(self, split_tokens: Optional[int] = None, nbytes: Optional[int] = None):
+        import torch
+        self.shape = self.make_shape(split_tokens)
+        if nbytes is None:
+            nbytes = paged_decode_attn_workspace_bytes(self.shape, self.max_seq_len)
+        self.workspace = torch.empty(int(nbytes), dtype=torch.uint8, device=self.q.device)
+        return self.workspace
+
+    # --- the three steps of one decode step --------------------------------
+    def write_step(self, stream=None):
+        """Write each sequence's newest token (position len-1) again."""
+        if self.step_k is None:
+            return
+        S, P = self.cfg.page_size, self.batch.num_pages
+        if self.kv_dtype == KV_FP8_E4M3:
+            if self.cfg.v_in_k:
+                kv_write_fp8(self.step_k, None, self.step_slots, self.k_cache, None,
+                             page_size=S, num_pages=P, scale_mode=SCALE_PER_TOKEN,
+                             token_scale=self.k_scale, stream=stream)
+            else:
+                kv_write_fp8(self.step_k, self.step_v, self.step_slots, self.k_cache,
+                             self.v_cache, page_size=S, num_pages=P,
+                             scale_mode=SCALE_PER_HEAD, k_scale=self.k_scale,
+                             v_scale=self.v_scale, stream=stream)
+        else:
+            kv_write_bf16(self.step_k, self.step_v, self.step_slots, self.k_cache,
+                          self.v_cache, page_size=S, num_pages=P, stream=stream)
+
+    def validate(self, stream=None):
+        validate_page_tags(self.page_tags, self.block_table, self.expected_tags,
+                           self.seq_lens, self.verdict, page_size=self.cfg.page_size,
+                           stream=stream)
+
+    def attend(self, use_verdict: bool = True, stream=None):
+        if self.workspace is None:
+            self.alloc_workspace()
+        ks = self.k_scale if self.kv_dtype == KV_FP8_E4M3 else None
+        vs = (self.v_scale if (self.kv_dtype == KV_FP8_E4M3 and not self.cfg.v_in_k)
+              else None)
+        paged_decode_attn(self.shape, self.q, self.k_cache, self.v_cache, ks, vs,
+                          self.block_table, self.seq_lens, self.max_seq_len,
+                          self.verdict if use_verdict else None, self.workspace, self.out,
+                          stream=stream)
+
+    def step(self, use_verdict: bool = True, stream=None):
+        self.write_step(stream)
+        if use_verdict:
+            self.validate(stream)
+        self.attend(use_verdict, stream)
+
+
+def build(batch: synth.Batch, kv_dtype: int, *, device: str = "cuda", data=None,
+          poison: bool = True, threads: Optional[int] = None) -> DeviceBatch:
+    """Allocate caches for `batch`, poison them, and write every context
+    token through the kv_write kernel. data: optional list of per-sequence
+    (k, v) bf16 arrays already generated (else generated here)."""
+    import torch
+    cfg = batch.cfg
+    B, P, S = batch.B, batch.num_pages, cfg.page_size
+    hkv, dk, dv = cfg.num_kv_heads, cfg.head_dim_qk, cfg.head_dim_v
+    fp8 = kv_dtype == KV_FP8_E4M3
+    if data is None:
+        data = synth.map_seqs(lambda s: batch.kv(s), list(range(B)), threads)
+    cdt = torch.uint8 if fp8 else torch.int16
+    fill = synth.poison_value(synth.KV_FP8 if fp8 else synth.KV_BF16)
+    if not fp8 and fill >= 0x8000:
+        fill -= 0x10000
+    k_cache = torch.full((P * hkv * S * dk,), fill if poison else 0, dtype=cdt, device=device)
+    v_cache = None
+    if not cfg.v_in_k:
+        v_cache = torch.full((P * hkv * S * dv,), fill if poison else 0, dtype=cdt, device=device)
+    host_scales = (None, None)
+    if fp8 and cfg.v_in_k:
+        k_scale = torch.full((P * S,), float("nan"), dtype=torch.float32, device=device)
+        v_scale = None
+    elif fp8:
+        hkam = np.zeros(hkv, np.float32)
+        hvam = np.zeros(hkv, np.float32)
+        for k, v in data:
+            if len(k):
+                hkam = np.maximum(hkam, np.abs(synth.bf16_to_f32(k)).max(axis=(0, 2)))
+                hvam = np.maximum(hvam, np.abs(synth.bf16_to_f32(v)).max(axis=(0, 2)))
+        ks = np.where(hkam > 0, hkam / np.float32(448), np.float32(1)).astype(np.float32)
+        vs = np.where(hvam > 0, hvam / np.float32(448), np.float32(1)).astype(np.float32)
+        host_scales = (ks, vs)
+        k_scale = torch.from_numpy(ks).to(device)
+        v_scale = torch.from_numpy(vs).to(device)
+    else:
+        k_scale = v_scale = None
+    db = DeviceBatch(
+        batch=batch, kv_dtype=kv_dtype,
+        q=_u16(torch, batch.q).to(device),
+        k_cache=k_cache, v_cache=v_cache, k_scale=k_scale, v_scale=v_scale,
+        block_table=torch.from_numpy(batch.block_table).to(device),
+        expected_tags=torch.from_numpy(batch.expected_tags.view(np.int32)).to(device),
+        page_tags=torch.from_numpy(batch.page_tags.view(np.int32)).to(device),
+        seq_lens=torch.from_numpy(batch.seq_lens).to(device),
+        verdict=torch.zeros(B, dtype=torch.int32, device=device),
+        out=torch.empty((B, cfg.num_q_heads, dv), dtype=torch.float32, device=device),
+        host_scales=host_scales)
+    # write the context, a few sequences per launch
+    pending = []
+    ntok = 0
+    for s in range(B):
+        l = int(batch.seq_lens[s])
+        if l == 0:
+            continue
+        pending.append(s)
+        ntok += l
+        if ntok >= 1 << 18 or s == B - 1:
+            _write_seqs(db, data, pending)
+            pending, ntok = [], 0
+    if pending:
+        _write_seqs(db, data, pending)
+    # the per-step token: position len-1 of every non-empty sequence
+    steps = [s for s in range(B) if batch.seq_lens[s] > 0]
+    if steps:
+        ks_ = np.stack([data[s][0][int(batch.seq_lens[s]) - 1] for s in steps])
+        db.step_k = _u16(torch, ks_).to(device)
+        if not cfg.v_in_k:
+            vs_ = np.stack([data[s][1][int(batch.seq_lens[s]) - 1] for s in steps])
+            db.step_v = _u16(torch, vs_).to(device)
+        sl = np.array([batch.slots(s, [int(batch.seq_lens[s]) - 1])[0] for s in steps],
+                      np.int64)
+        db.step_slots = torch.from_numpy(sl).to(device)
+    torch.cuda.synchronize()
+    return db
+
+
+def _write_seqs(db: DeviceBatch, data, seqs):
+    import torch
+    batch = db.batch
+    device = db.q.device
+    k = np.concatenate([data[s][0] for s in seqs])
+    slots = np.concatenate([batch.slots(s, np.arange(int(batch.seq_lens[s]))) for s in seqs])
+    kt = _u16(torch, k).to(device)
+    st = torch.from_numpy(slots.astype(np.int64)).to(device)
+    S, P = db.cfg.page_size, batch.num_pages
+    if db.cfg.v_in_k:
+        vt = None
+    else:
+        vt = _u16(torch, np.concatenate([data[s][1] for s in seqs])).to(device)
+    if db.kv_dtype == KV_FP8_E4M3:
+        if db.cfg.v_in_k:
+            kv_write_fp8(kt, None, st, db.k_cache, None, page_size=S, num_pages=P,
+                         scale_mode=SCALE_PER_TOKEN, token_scale=db.k_scale)
+        else:
+            kv_write_fp8(kt, vt, st, db.k_cache, db.v_cache, page_size=S, num_pages=P,
+                         scale_mode=SCALE_PER_HEAD, k_scale=db.k_scale, v_scale=db.v_scale)
+    else:
+        kv_write_bf16(kt, vt, st, db.k_cache, db.v_cache, page_size=S, num_pages=P)
+
+
+def kv_bytes(batch: synth.Batch, kv_dtype: int) -> int:
+    """Algorithmic KV bytes one attention call reads: every context token of
+    every kv head, K and V (latent: the shared entry once) plus per-token
+    scales."""
+    cfg = batch.cfg
+    tokens = int(np.sum(batch.seq_lens.astype(np.int64)))
+    elem = 1 if kv_dtype == KV_FP8_E4M3 else 2
+    if cfg.v_in_k:
+        return tokens * (cfg.head_dim_qk * elem + (4 if kv_dtype == KV_FP8_E4M3 else 0))
+    return tokens * cfg.num_kv_heads * (cfg.head_dim_qk + cfg.head_dim_v) * elem
+
+
+def attention_flops(batch: synth.Batch) -> int:
+    cfg = batch.cfg
+    tokens = int(np.sum(batch.seq_lens.astype(np.int64)))
+    return 2 * cfg.num_q_heads * (cfg.head_dim_qk + cfg.head_dim_v) * tokens
+
