@@ -121,6 +121,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device-to-device copy, whose HBM "
+                         "counters calibrate FETCH_SIZE / WRITE_SIZE in a profiled run")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -136,6 +139,17 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     pda.load()
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
+        log("copy calibration: 1 GiB read + 1 GiB written by one copy kernel")
     batch = synth.make_batch(WORKLOAD_ID)
     cfg = batch.cfg
     log("generating inputs")

@@ -36,6 +36,7 @@
 // Every dot accumulates in fp32; q enters exactly (bf16), K and V codes
 // convert exactly, and p is rounded once (f16 nearest-even, or hi+lo bf16).
 #include <mutex>
+#include <type_traits>
 
 #include "pda_internal.h"
 
@@ -133,10 +134,12 @@ __device__ int build_plan(const AttnArgs& a, int S, int* pref, int* tmp, int& ch
   return total;
 }
 
-// Query rows are read through the constant address space, so uniform loads
-// become scalar loads into SGPRs. The 512 q dwords of a G = 8 group cannot
-// stay resident in SGPRs, so they are re-read every block in small chunks.
+// Query rows and block-table entries are read through the constant address
+// space, so wave-uniform loads become scalar loads into SGPRs. The 512 q
+// dwords of a G = 8 group cannot stay resident in SGPRs, so they are re-read
+// every block in small chunks.
 typedef const uint32_t __attribute__((address_space(4))) cu32_t;
+typedef const int32_t __attribute__((address_space(4))) ci32_t;
 
 // Opaque identity on the q pointer that also "uses and redefines" the score
 // accumulators: loads through the returned pointer cannot move above the dot
@@ -144,7 +147,9 @@ typedef const uint32_t __attribute__((address_space(4))) cu32_t;
 template <int R>
 __device__ __forceinline__ cu32_t* fence_ptr_after(cu32_t* p, float (&z)[R]) {
   uint64_t v = (uint64_t)(uintptr_t)p;
-  if constexpr (R == 2) {
+  if constexpr (R == 1) {
+    asm volatile("" : "+s"(v), "+v"(z[0]));
+  } else if constexpr (R == 2) {
     asm volatile("" : "+s"(v), "+v"(z[0]), "+v"(z[1]));
   } else if constexpr (R == 4) {
     asm volatile("" : "+s"(v), "+v"(z[0]), "+v"(z[1]), "+v"(z[2]), "+v"(z[3]));
@@ -155,20 +160,52 @@ __device__ __forceinline__ cu32_t* fence_ptr_after(cu32_t* p, float (&z)[R]) {
   return (cu32_t*)(uintptr_t)v;
 }
 
-template <int G, bool FP8, int S>
-struct ItemCtx {
-  static constexpr int R = G < 2 ? 2 : G;     // rows carried (padded to 2)
-  static constexpr int KQ = FP8 ? 8 : 16;     // uint4 of K per lane per block
-  static constexpr int VQ = FP8 ? 8 : 16;     // uint4 of V per lane per block
-  static constexpr int E = FP8 ? 1 : 2;       // bytes per element
+__device__ __forceinline__ uint32_t u4_get(const uint4& v, int j) {
+  return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
+// Bytes of the per-wave p buffer in LDS: G rows x 64 tokens of f16 (FP8
+// caches), or of a bf16 high part plus a bf16 remainder (BF16 caches).
+template <int G, bool FP8>
+constexpr int pbuf_bytes() {
+  return G * 64 * 2 * (FP8 ? 1 : 2);
+}
+
+// Physical page ids of the (up to four) pages one 64-token block spans, as
+// separate scalars (an indexed array here ends up in scratch memory).
+struct Pages {
+  int p0, p1, p2, p3;
+  __device__ __forceinline__ int get(int k) const {
+    return k == 0 ? p0 : k == 1 ? p1 : k == 2 ? p2 : p3;
+  }
+  __device__ __forceinline__ void set(int k, int v) {
+    if (k == 0) p0 = v; else if (k == 1) p1 = v; else if (k == 2) p2 = v; else p3 = v;
+  }
 };
 
 template <int G, bool FP8, int S>
-__device__ __forceinline__ void load_k(const AttnArgs& a, int g, int page, int off,
-                                       uint4 (&kk)[ItemCtx<G, FP8, S>::KQ]) {
-  using C = ItemCtx<G, FP8, S>;
+struct Item {
+  static constexpr int E = FP8 ? 1 : 2;        // bytes per cache element
+  static constexpr int NP = 64 / S;            // pages per 64-token block
+  static constexpr int KQ = 8 * E;             // 16-byte K vectors per lane per block
+  static constexpr int VW = E;                 // dwords of V per lane per token pair
+  using vword_t = typename std::conditional<FP8, uint32_t, uint2>::type;
+};
+
+// K of the lane's token (lane = token b0 + lane) for one 64-token block:
+// the token's 128 dims as eight 16-dim column groups.
+template <int G, bool FP8, int S>
+__device__ __forceinline__ void load_k(const AttnArgs& a, int g, const Pages& pg,
+                                       uint4 (&kk)[Item<G, FP8, S>::KQ]) {
+  using I = Item<G, FP8, S>;
+  const int lane = __lane_id();
+  // page of the lane's token, from wave-uniform ids with arithmetic only
+  int page = pg.p0;
+  if constexpr (I::NP >= 2) page += (lane >= S) * (pg.p1 - pg.p0);
+  if constexpr (I::NP >= 4) page += (lane >= 2 * S) * (pg.p2 - pg.p1) + (lane >= 3 * S) * (pg.p3 - pg.p2);
+  const int off = lane % S;
   // element (page, g, off, 16c + i) at (((page*Hkv + g)*8 + c)*S + off)*16 + i
-  const uint8_t* base = a.kc + ((((int64_t)page * a.Hkv + g) * 8) * S + off) * 16 * C::E;
+  const uint8_t* base = a.kc + ((((int64_t)page * a.Hkv + g) * 8) * S + off) * 16 * I::E;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     if constexpr (FP8) {
@@ -180,303 +217,331 @@ __device__ __forceinline__ void load_k(const AttnArgs& a, int g, int page, int o
   }
 }
 
+// V of one 64-token block for the lane's two dims (2*lane, 2*lane+1): one
+// word per token pair. In the V format the pair row (page, g, off/2) holds
+// (dim d, token off) at element 2*d + off%2, so dims 2l and 2l+1 of both
+// tokens are the four consecutive elements 4l..4l+3.
 template <int G, bool FP8, int S>
-__device__ __forceinline__ void load_v(const AttnArgs& a, int g, int page, int off0, int tt,
-                                       uint4 (&vv)[ItemCtx<G, FP8, S>::VQ]) {
-  using C = ItemCtx<G, FP8, S>;
-  // element (page, g, off, d) at
-  //   (page*Hkv + g)*S*128 + ((off/2)*16 + d/8)*16 + (d%8)*2 + off%2
-  const uint8_t* base = a.vc + (((int64_t)page * a.Hkv + g) * S * kD +
-                                ((int64_t)(off0 / 2) * 16 + tt) * 16) * C::E;
+__device__ __forceinline__ void load_v(const AttnArgs& a, int g, const Pages& pg,
+                                       typename Item<G, FP8, S>::vword_t (&vv)[32]) {
+  using I = Item<G, FP8, S>;
+  using W = typename I::vword_t;
+  const int lane = __lane_id();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if constexpr (FP8) {
-      vv[i] = *reinterpret_cast<const uint4*>(base + i * 256);
-    } else {
-      vv[2 * i] = *reinterpret_cast<const uint4*>(base + i * 512);
-      vv[2 * i + 1] = *reinterpret_cast<const uint4*>(base + i * 512 + 16);
-    }
+  for (int i = 0; i < 32; ++i) {
+    const int page = pg.get((2 * i) / S);
+    const int pr = ((2 * i) % S) / 2;
+    const uint8_t* row = a.vc + (((int64_t)page * a.Hkv + g) * (S / 2) + pr) * (kD * 2) * I::E;
+    vv[i] = *reinterpret_cast<const W*>(row + lane * 4 * I::E);
   }
 }
 
-__device__ __forceinline__ uint32_t u4_get(const uint4& v, int j) {
-  return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+// PV of one 64-token block for the lane's two dims: acc[r][0..1] +=
+// sum over token pairs of (p pair of row r) . (V pair of dim 2l / 2l+1).
+// Step k = (ic, r) takes row r's four p pairs of token pairs 4ic..4ic+3 in
+// one 16-byte LDS read (a wave-uniform address, so a broadcast). Reads run
+// kPD steps ahead of their use.
+constexpr int kPD = 4;
+
+__device__ __forceinline__ uint32_t word0(uint32_t w) { return w; }
+__device__ __forceinline__ uint32_t word0(uint2 w) { return w.x; }
+
+// Mask keeping the elements of tokens (2i, 2i+1) that are below `valid`, for
+// a word holding one 16-bit value of each token (low half: token 2i).
+__device__ __forceinline__ uint32_t pair_mask(int i, int valid) {
+  return (2 * i < valid ? 0x0000FFFFu : 0u) | (2 * i + 1 < valid ? 0xFFFF0000u : 0u);
+}
+
+// The same for a word of four e4m3 codes (dim 2l: tokens 2i, 2i+1, then
+// dim 2l+1: tokens 2i, 2i+1).
+__device__ __forceinline__ uint32_t code_pair_mask(int i, int valid) {
+  return (2 * i < valid ? 0x00FF00FFu : 0u) | (2 * i + 1 < valid ? 0xFF00FF00u : 0u);
+}
+
+template <int G, bool FP8, bool TAIL>
+__device__ __forceinline__ void pv_block(
+    const typename std::conditional<FP8, uint32_t, uint2>::type (&vv)[32], const uint16_t* pw,
+    float (&acc)[G][2], int valid) {
+  constexpr int NK = 8 * G;
+  constexpr int D = NK < kPD ? NK : kPD;
+  auto rd = [&](int k, int part) -> uint4 {
+    const int ic = k / G, r = k % G;
+    return *reinterpret_cast<const uint4*>(pw + part * G * 64 + r * 64 + ic * 8);
+  };
+  uint4 ph[D], pl[D];
+#pragma unroll
+  for (int k = 0; k < D; ++k) {
+    ph[k] = rd(k, 0);
+    if constexpr (!FP8) pl[k] = rd(k, 1);
+  }
+  f16x2_t v0[4], v1[4];
+  static_for<0, NK>::run([&](auto K) {
+    constexpr int k = decltype(K)::value;
+    constexpr int ic = k / G, r = k % G;
+    if constexpr (FP8 && r == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t w = word0(vv[4 * ic + j]);
+        // bytes: (dim 2l, token 2i), (2l, 2i+1), (2l+1, 2i), (2l+1, 2i+1)
+        if constexpr (TAIL) w &= code_pair_mask(4 * ic + j, valid);
+        v0[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+        v1[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+      }
+    }
+    const uint4 ch = ph[k % D];
+    uint4 cl = ch;
+    if constexpr (!FP8) cl = pl[k % D];
+    if constexpr (k + D < NK) {
+      ph[k % D] = rd(k + D, 0);
+      if constexpr (!FP8) pl[k % D] = rd(k + D, 1);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (FP8) {
+        const f16x2_t p2 = __builtin_bit_cast(f16x2_t, u4_get(ch, j));
+        acc[r][0] = __builtin_amdgcn_fdot2(p2, v0[j], acc[r][0], false);
+        acc[r][1] = __builtin_amdgcn_fdot2(p2, v1[j], acc[r][1], false);
+      } else {
+        const bf16x2_t hi = __builtin_bit_cast(bf16x2_t, u4_get(ch, j));
+        const bf16x2_t lo = __builtin_bit_cast(bf16x2_t, u4_get(cl, j));
+        uint32_t wa = vv[4 * ic + j].x, wb = vv[4 * ic + j].y;
+        if constexpr (TAIL) {
+          const uint32_t msk = pair_mask(4 * ic + j, valid);
+          wa &= msk;
+          wb &= msk;
+        }
+        const bf16x2_t va = __builtin_bit_cast(bf16x2_t, wa);
+        const bf16x2_t vb = __builtin_bit_cast(bf16x2_t, wb);
+        acc[r][0] = __builtin_amdgcn_fdot2_f32_bf16(hi, va, acc[r][0], false);
+        acc[r][0] = __builtin_amdgcn_fdot2_f32_bf16(lo, va, acc[r][0], false);
+        acc[r][1] = __builtin_amdgcn_fdot2_f32_bf16(hi, vb, acc[r][1], false);
+        acc[r][1] = __builtin_amdgcn_fdot2_f32_bf16(lo, vb, acc[r][1], false);
+      }
+    }
+    // keep the schedule in program order: otherwise every conversion and
+    // LDS read of the block is hoisted to the top, a register each
+    __builtin_amdgcn_sched_barrier(0);
+  });
 }
 
 template <int G, bool FP8, int S>
-__device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, long long item) {
-  using C = ItemCtx<G, FP8, S>;
-  constexpr int R = C::R;
+__device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, long long item,
+                             uint16_t* pw) {
+  using I = Item<G, FP8, S>;
+  using W = typename I::vword_t;
+  constexpr int NP = I::NP;
   const int lane = __lane_id();
-  const int tg = lane >> 4;
-  const int tt = lane & 15;
   const int len = a.lens[s];
   const int tok0 = c * chunk;
   const int tok1 = min(len, tok0 + chunk);
-  const int32_t* btrow = a.bt + (int64_t)s * a.max_blocks;
-  cu32_t* qbase =
-      (cu32_t*)(uintptr_t)(a.q + ((int64_t)s * a.Hq + (int64_t)g * G) * kD);
+  ci32_t* btrow = (ci32_t*)(uintptr_t)(a.bt + (int64_t)s * a.max_blocks);
+  cu32_t* qbase = (cu32_t*)(uintptr_t)(a.q + ((int64_t)s * a.Hq + (int64_t)g * G) * kD);
   const float kmul = a.sm_scale * (FP8 ? a.k_scale[g] : 1.0f) * kLog2e;
-  // v_perm selector building the p pair of this lane (see pack below)
-  const uint32_t sel_f16 = (tt & 1) ? 0x03020706u : 0x05040100u;
 
-  float m[R], l[R], acc[R][8];
+  float m[G], l[G], acc[G][2];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
+  for (int r = 0; r < G; ++r) {
     m[r] = -INFINITY;
     l[r] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[r][j] = 0.0f;
+    acc[r][0] = acc[r][1] = 0.0f;
   }
   bool bad = false;
 
-  // Physical page of this lane's 16-token group in the block starting at b0.
-  // Groups past the end of the chunk read the chunk's first page instead (a
-  // page of this sequence); their tokens are masked out below. A page id
-  // outside [0, P) is never dereferenced: it marks the item bad.
+  // Physical pages of the block starting at b0 (wave-uniform). Pages past the
+  // end of the chunk are replaced by the chunk's first page, a page of this
+  // sequence; their tokens are masked out below. A page id outside [0, P) is
+  // never dereferenced: it marks the item bad.
   int fb = btrow[tok0 / S];
   if (fb < 0 || fb >= a.P) {
     bad = true;
     fb = 0;
   }
-  auto page_of = [&](int b0) -> int {
-    const int gtok = b0 + 16 * tg;
-    int p = fb;
-    if (gtok < tok1) {
-      p = btrow[gtok / S];
-      if (p < 0 || p >= a.P) {
-        bad = true;
-        p = fb;
+  auto pages_of = [&](int b0, Pages& pg) {
+    pg.p1 = pg.p2 = pg.p3 = fb;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      const int t = b0 + k * S;
+      int p = fb;
+      if (t < tok1) {
+        p = btrow[t / S];
+        if (p < 0 || p >= a.P) {
+          bad = true;
+          p = fb;
+        }
       }
+      pg.set(k, p);
     }
-    return p;
   };
 
-  uint4 kk[C::KQ];
-  uint4 vv[C::VQ];
+  uint4 kk[I::KQ];
+  W vv[32];
+  Pages pg;
   int b0 = tok0;
-  {
-    const int page = page_of(b0);
-    load_k<G, FP8, S>(a, g, page, (b0 + 16 * tg) % S + tt, kk);
-    load_v<G, FP8, S>(a, g, page, (b0 + 16 * tg) % S, tt, vv);
-  }
+  pages_of(b0, pg);
+  load_k<G, FP8, S>(a, g, pg, kk);
+  load_v<G, FP8, S>(a, g, pg, vv);
 
   for (;;) {
     const int bn = b0 + 64;
     const bool has_next = bn < tok1;
-    int npage = 0;
-    if (has_next) npage = page_of(bn);
+    const bool tail = b0 + 64 > tok1;
+    Pages npg = pg;
+    if (has_next) pages_of(bn, npg);
 
     // ---- QK: lane = token b0 + lane ------------------------------------
     // Eight dims (four q pairs per row) at a time, q in SGPRs. The loads of
     // chunk c+2 are released by a fence that consumes the scores produced by
     // chunk c, so exactly two 4-pair chunks of q are live at any time.
-    const bool tok_ok = (b0 + lane) < tok1;
-    float z[R];
+    float z[G];
 #pragma unroll
-    for (int r = 0; r < R; ++r) z[r] = 0.0f;
+    for (int r = 0; r < G; ++r) z[r] = 0.0f;
     {
-      uint32_t qbuf[2][G][4];
-      auto loadq = [&](int cc8, uint32_t(&dst)[G][4]) {
-        cu32_t* qp = fence_ptr_after<R>(qbase, z);
+      uint32_t qbuf[2][G][2];
+      auto loadq = [&](int c4, uint32_t(&dst)[G][2]) {
+        cu32_t* qp = fence_ptr_after<G>(qbase, z);
 #pragma unroll
         for (int r = 0; r < G; ++r)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) dst[r][j] = qp[r * 64 + cc8 * 4 + j];
+          for (int j = 0; j < 2; ++j) dst[r][j] = qp[r * 64 + c4 * 2 + j];
       };
       loadq(0, qbuf[0]);
       loadq(1, qbuf[1]);
-      static_for<0, 16>::run([&](auto CC) {
-        constexpr int cc8 = decltype(CC)::value;
-        bf16x2_t kp[4];
-        if constexpr (FP8) {
-          const uint32_t c0 = u4_get(kk[cc8 >> 1], (cc8 & 1) * 2);
-          const uint32_t c1 = u4_get(kk[cc8 >> 1], (cc8 & 1) * 2 + 1);
-          kp[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, 1.0f, false);
-          kp[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, 1.0f, true);
-          kp[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, 1.0f, false);
-          kp[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, 1.0f, true);
-        } else {
+      bf16x2_t kp[4];
+      static_for<0, 32>::run([&](auto CC) {
+        constexpr int c4 = decltype(CC)::value;   // dims 4*c4 .. 4*c4+3
+        if constexpr ((c4 & 1) == 0) {
+          constexpr int c8 = c4 >> 1;             // dims 8*c8 .. 8*c8+7
+          if constexpr (FP8) {
+            const uint32_t w0 = u4_get(kk[c8 >> 1], (c8 & 1) * 2);
+            const uint32_t w1 = u4_get(kk[c8 >> 1], (c8 & 1) * 2 + 1);
+            kp[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+            kp[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+            kp[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+            kp[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+          } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) kp[j] = __builtin_bit_cast(bf16x2_t, u4_get(kk[cc8], j));
+            for (int j = 0; j < 4; ++j) kp[j] = __builtin_bit_cast(bf16x2_t, u4_get(kk[c8], j));
+          }
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int r = 0; r < G; ++r)
             z[r] = __builtin_amdgcn_fdot2_f32_bf16(
-                __builtin_bit_cast(bf16x2_t, qbuf[cc8 & 1][r][j]), kp[j], z[r], false);
-        if constexpr (cc8 + 2 < 16) loadq(cc8 + 2, qbuf[cc8 & 1]);
+                __builtin_bit_cast(bf16x2_t, qbuf[c4 & 1][r][j]), kp[(c4 & 1) * 2 + j], z[r],
+                false);
+        if constexpr (c4 + 2 < 32) loadq(c4 + 2, qbuf[c4 & 1]);
+        if constexpr ((c4 & 1) == 1) __builtin_amdgcn_sched_barrier(0);
       });
     }
     // K registers are free: prefetch the next block's keys.
-    if (has_next)
-      load_k<G, FP8, S>(a, g, npage, (bn + 16 * tg) % S + tt, kk);
+    if (has_next) load_k<G, FP8, S>(a, g, npg, kk);
 
-    // ---- online softmax ------------------------------------------------
-    float zl[R], p[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) zl[r] = (tok_ok && r < G) ? z[r] * kmul : -INFINITY;
-    bool need = false;
-    float bm[R];
+    // ---- online softmax (log2 units) -----------------------------------
+    // zl = z*kmul - m. The running max m only moves when some score of the
+    // block exceeds it by more than kTau, so p = 2^zl <= 2^kTau and the
+    // exact block maximum (a wave reduction) is only taken in that case.
+    const bool tok_ok = (b0 + lane) < tok1;
+    float zl[G];
+    uint64_t over = 0;
 #pragma unroll
     for (int r = 0; r < G; ++r) {
-      bm[r] = wave_max(zl[r]);
-      need |= bm[r] > m[r] + kTau;
+      zl[r] = fmaf(z[r], kmul, -m[r]);
+      if (tail && !tok_ok) zl[r] = -INFINITY;
+      over |= __ballot(zl[r] > kTau);
     }
-    if (need) {
+    if (over != 0) {
 #pragma unroll
       for (int r = 0; r < G; ++r) {
-        if (bm[r] > m[r] + kTau) {
-          const float alpha = exp2f(m[r] - bm[r]);
-          m[r] = bm[r];
+        if (__ballot(zl[r] > kTau) != 0) {
+          const float bm = wave_max((tail && !tok_ok) ? -INFINITY : z[r] * kmul);
+          const float alpha = __builtin_amdgcn_exp2f(m[r] - bm);
+          m[r] = bm;
           l[r] *= alpha;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[r][j] *= alpha;
+          acc[r][0] *= alpha;
+          acc[r][1] *= alpha;
+          zl[r] = (tail && !tok_ok) ? -INFINITY : fmaf(z[r], kmul, -bm);
         }
       }
     }
+    // p of this lane's token for every row, to the wave's LDS buffer:
+    // pw[r*64 + t] (f16), or hi/lo bf16 parts at pw and pw + G*64.
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      p[r] = (r < G) ? exp2f(zl[r] - m[r]) : 0.0f;
-      l[r] += p[r];
-    }
-
-    // ---- pack p pairs along tokens --------------------------------------
-    // Lane tt holds p of token tt for every row. Even lanes build
-    // (p[r][tt], p[r][tt+1]) for rows r < R/2, odd lanes build
-    // (p[r][tt-1], p[r][tt]) for rows r >= R/2.
-    constexpr int H = R / 2;
-    uint32_t pp[H], pplo[H];
-#pragma unroll
-    for (int j = 0; j < H; ++j) {
+    for (int r = 0; r < G; ++r) {
+      const float p = __builtin_amdgcn_exp2f(zl[r]);
+      l[r] += p;
       if constexpr (FP8) {
-        const f16x2_t hv = {(_Float16)p[j], (_Float16)p[j + H]};
-        const uint32_t mine = __builtin_bit_cast(uint32_t, hv);
-        const uint32_t nb = dpp_u32<DPP_QUAD_1032>(mine);
-        pp[j] = __builtin_amdgcn_perm(nb, mine, sel_f16);
+        pw[r * 64 + lane] = __builtin_bit_cast(uint16_t, (_Float16)p);
       } else {
-        // hi = bf16 truncation of p, lo = bf16 truncation of the remainder
-        const uint32_t b0u = as_u32(p[j]), b1u = as_u32(p[j + H]);
-        const float r0 = p[j] - as_f32(b0u & 0xFFFF0000u);
-        const float r1 = p[j + H] - as_f32(b1u & 0xFFFF0000u);
-        const uint32_t mine_hi = __builtin_amdgcn_perm(b1u, b0u, 0x07060302u);
-        const uint32_t mine_lo = __builtin_amdgcn_perm(as_u32(r1), as_u32(r0), 0x07060302u);
-        const uint32_t nb_hi = dpp_u32<DPP_QUAD_1032>(mine_hi);
-        const uint32_t nb_lo = dpp_u32<DPP_QUAD_1032>(mine_lo);
-        pp[j] = __builtin_amdgcn_perm(nb_hi, mine_hi, sel_f16);
-        pplo[j] = __builtin_amdgcn_perm(nb_lo, mine_lo, sel_f16);
+        const uint32_t pu = as_u32(p);
+        const float rem = p - as_f32(pu & 0xFFFF0000u);
+        pw[r * 64 + lane] = (uint16_t)(pu >> 16);
+        pw[G * 64 + r * 64 + lane] = (uint16_t)(as_u32(rem) >> 16);
       }
     }
+    // The wave's own LDS writes above must land before its reads below.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // ---- PV: lane = (token group tg, dims 8tt..8tt+7) --------------------
-    if (!(b0 + 64 <= tok1)) {
-      // tail block: zero V codes of tokens at or beyond tok1
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int t0 = b0 + 16 * tg + 2 * i;
-        const bool v0 = t0 < tok1, v1 = t0 + 1 < tok1;
-        const uint32_t msk = FP8 ? ((v0 ? 0x00FF00FFu : 0u) | (v1 ? 0xFF00FF00u : 0u))
-                                 : ((v0 ? 0x0000FFFFu : 0u) | (v1 ? 0xFFFF0000u : 0u));
-        if constexpr (FP8) {
-          vv[i].x &= msk; vv[i].y &= msk; vv[i].z &= msk; vv[i].w &= msk;
-        } else {
-          vv[2 * i].x &= msk; vv[2 * i].y &= msk; vv[2 * i].z &= msk; vv[2 * i].w &= msk;
-          vv[2 * i + 1].x &= msk; vv[2 * i + 1].y &= msk;
-          vv[2 * i + 1].z &= msk; vv[2 * i + 1].w &= msk;
-        }
-      }
+    // ---- PV: lane = dims (2*lane, 2*lane+1), all 64 tokens ---------------
+    // In the tail block, tokens at or beyond tok1 have p = 0 but their V
+    // codes may be stale or poisoned (NaN * 0 = NaN): they are zeroed after
+    // conversion, in a separate instantiation of the loop.
+    // (the empty asm keeps the two copies from being merged back into one)
+    if (tail) {
+      asm volatile("" ::: "memory");
+      pv_block<G, FP8, true>(vv, pw, acc, tok1 - b0);
+    } else {
+      asm volatile("" ::: "memory");
+      pv_block<G, FP8, false>(vv, pw, acc, 64);
     }
-    static_for<0, 8>::run([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      uint32_t pb[R], pbl[R];
-#pragma unroll
-      for (int r = 0; r < H; ++r) {
-        pb[r] = dpp_u32<DPP_ROW_NEWBCAST0 + 2 * i>(pp[r]);
-        pb[r + H] = dpp_u32<DPP_ROW_NEWBCAST0 + 2 * i + 1>(pp[r]);
-        if constexpr (!FP8) {
-          pbl[r] = dpp_u32<DPP_ROW_NEWBCAST0 + 2 * i>(pplo[r]);
-          pbl[r + H] = dpp_u32<DPP_ROW_NEWBCAST0 + 2 * i + 1>(pplo[r]);
-        }
-      }
-      if constexpr (FP8) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t code4 = u4_get(vv[i], w);
-          const f16x2_t va = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code4, 1.0f, false);
-          const f16x2_t vb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code4, 1.0f, true);
-#pragma unroll
-          for (int r = 0; r < G; ++r) {
-            const f16x2_t ph = __builtin_bit_cast(f16x2_t, pb[r]);
-            acc[r][2 * w] = __builtin_amdgcn_fdot2(ph, va, acc[r][2 * w], false);
-            acc[r][2 * w + 1] = __builtin_amdgcn_fdot2(ph, vb, acc[r][2 * w + 1], false);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int jd = 0; jd < 8; ++jd) {
-          const bf16x2_t vp = __builtin_bit_cast(bf16x2_t, u4_get(vv[2 * i + (jd >> 2)], jd & 3));
-#pragma unroll
-          for (int r = 0; r < G; ++r) {
-            acc[r][jd] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pb[r]), vp,
-                                                         acc[r][jd], false);
-            acc[r][jd] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pbl[r]), vp,
-                                                         acc[r][jd], false);
-          }
-        }
-      }
-    });
     if (!has_next) break;
-    load_v<G, FP8, S>(a, g, npage, (bn + 16 * tg) % S, tt, vv);
+    load_v<G, FP8, S>(a, g, npg, vv);
+    pg = npg;
     b0 = bn;
+    // the next block's p writes must not pass this block's p reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
   // ---- write the partial ------------------------------------------------
   float* part = a.ws_part + item * (int64_t)(G * (kD + 2));
-  const bool item_bad = __ballot(bad) != 0;
-  if (item_bad) {
+  if (bad) {
     if (lane < G) part[G * kD + lane] = __builtin_nanf("");
     return;
   }
-  float ltot[G];
-#pragma unroll
-  for (int r = 0; r < G; ++r) ltot[r] = wave_sum(l[r]);
 #pragma unroll
   for (int r = 0; r < G; ++r) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float x = acc[r][j];
-      x += shfl_xor_f32(x, 16);
-      x += shfl_xor_f32(x, 32);
-      acc[r][j] = x;
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < G; ++r) {
-    if ((r & 3) == tg) {
-      float4* dst = reinterpret_cast<float4*>(part + r * kD + 8 * tt);
-      dst[0] = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
-      dst[1] = make_float4(acc[r][4], acc[r][5], acc[r][6], acc[r][7]);
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < G; ++r) {
+    const float lt = wave_sum(l[r]);
+    *reinterpret_cast<float2*>(part + r * kD + 2 * lane) = make_float2(acc[r][0], acc[r][1]);
     if (lane == r) {
       part[G * kD + r] = m[r];
-      part[G * kD + G + r] = ltot[r];
+      part[G * kD + G + r] = lt;
     }
   }
 }
 
+// Waves per SIMD the register allocator must leave room for.
+template <int G, bool FP8>
+constexpr int partial_waves() {
+  return FP8 ? 3 : 2;
+}
+
 template <int G, bool FP8, int S>
-__global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a) {
-  extern __shared__ int lds[];
-  int* tmp = lds;                    // kThreads + 1
-  int* pref = lds + kThreads + 1;    // B + 1
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(partial_waves<G, FP8>(), partial_waves<G, FP8>())))
+void attn_partial_kernel(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) int lds[];
+  constexpr int PB = pbuf_bytes<G, FP8>();
+  const int wave = threadIdx.x >> 6;
+  uint16_t* pw = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(lds) + wave * PB);
+  int* tmp = lds + kWaves * PB / 4;   // kThreads + 1
+  int* pref = tmp + kThreads + 1;     // B + 1
   int chunk;
   const int total_sc = build_plan(a, S, pref, tmp, chunk);
   const long long total_items = (long long)total_sc * a.Hkv;
-  const int wave = threadIdx.x >> 6;
   const long long nw = (long long)gridDim.x * kWaves;
   for (long long item = (long long)blockIdx.x * kWaves + wave; item < total_items; item += nw) {
     const int sc = (int)(item / a.Hkv);
@@ -489,7 +554,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnArgs a) {
     }
     const int s = __builtin_amdgcn_readfirstlane(lo);
     const int c = __builtin_amdgcn_readfirstlane(sc - pref[lo]);
-    process_item<G, FP8, S>(a, s, c, __builtin_amdgcn_readfirstlane(g), chunk, item);
+    process_item<G, FP8, S>(a, s, c, __builtin_amdgcn_readfirstlane(g), chunk, item, pw);
   }
 }
 
@@ -747,7 +812,8 @@ extern "C" int paged_decode_attn(const pda_attn_shape* shape, const void* q, con
 
   const kernel_t pk = fp8 ? pick_partial<true>(G, sh.page_size) : pick_partial<false>(G, sh.page_size);
   const combine_t ck = fp8 ? pick_combine<true>(G) : pick_combine<false>(G);
-  const size_t lds = (size_t)(kThreads + 1 + sh.num_seqs + 1) * sizeof(int);
+  const size_t pbuf = (size_t)kWaves * (size_t)(fp8 ? 1 : 2) * (size_t)G * 64 * 2;
+  const size_t lds = pbuf + (size_t)(kThreads + 1 + sh.num_seqs + 1) * sizeof(int);
   const long long ml = max_seq_len > 0 ? max_seq_len : 1;
   const long long items_bound = (long long)sh.num_seqs * sh.num_kv_heads * ((ml + chunk - 1) / chunk);
   long long grid = (long long)device_cu_count() * blocks_per_cu(pk, lds);
