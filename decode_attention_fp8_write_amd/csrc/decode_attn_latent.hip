@@ -1,30 +1,590 @@
-// decode_attn_latent.hip — latent-cache decode attention (one kv head whose
-// first Dv dims double as the value vector, per-token scales, >= 16 query
-// rows per kv head) on MFMA. Not built yet: the entry points report the
-// shape as unsupported.
+// decode_attn_latent.hip — decode attention over a latent paged cache on
+// MFMA: one kv head whose 576-dim FP8 entry is the key and whose first 512
+// dims are the value, one fp32 scale per token, and 32..128 query heads
+// sharing it, so every page is a dense (heads x tokens) contraction.
+//
+// The pages state that the cache is kept as 8-bit e4m3 and that the
+// attention kernel converts what it reads (aifeed.sk, "Cloudflare zrýchľuje
+// inferenciu modelov Kimi a GLM kompresiou cache a váh", section "Dve odlišné
+// úzke miesta v pamäti GPU"; manulx.blog, "Công thức của Cloudflare để phục
+// vụ Kimi và GLM", section "Bộ nhớ đệm KV FP8 tăng gấp đôi dung lượng ngữ
+// cảnh"). The kernel design is not from the pages, which give none.
+//
+// Work split. The valid pages of all non-aborted sequences are laid end to
+// end and cut into one equal range per workgroup (a flat split, so long and
+// short sequences balance). A workgroup walks the fragments of sequences in
+// its range; each fragment leaves one partial (unnormalised output rows, a
+// running max and a running weight sum per head) in workspace slot
+// (workgroup + sequence), which is unique. The combine kernel merges the
+// fragments of each sequence with a log-sum-exp rule.
+//
+// Inside a fragment, one page (64 tokens) at a time:
+//  * the workgroup copies the page's 36 KB of codes and its 64 scales into
+//    LDS (double-buffered: the next page is fetched into registers while the
+//    current one is computed). Tokens past the end are written as zero codes
+//    with weight 0, so they contribute nothing and poisoned bytes are never
+//    read into the arithmetic.
+//  * wave w owns query heads [32w, 32w+32). QK as S^T = K Q^T on
+//    v_mfma_f32_32x32x16_bf16: K codes convert exactly to bf16 (A operand,
+//    lane = token), Q stays resident in registers as bf16 (B operand, lane =
+//    head), so Q enters exactly.
+//  * softmax in log2 units with the per-token scale folded in: for token t
+//    with scale c_t, y = (q.code_t) * c_t * sm_scale * log2(e) + log2(c_t);
+//    p' = 2^(y - m) = c_t * e^(score - m'), so the weights already carry the
+//    value scale, and the running sum adds p' / c_t. The running max m only
+//    moves when a page's max exceeds it by more than 8 (p' <= 2^8).
+//  * PV as O^T = V^T P^T on v_mfma_f32_32x32x16_f16: V codes convert exactly
+//    to f16. The A operand needs eight tokens of one dim per lane; the LDS
+//    transpose read ds_read_b64_tr_b8 gathers them from the token-major page
+//    (in each 16-lane group, lane i receives byte i%8 of the eight 8-byte
+//    chunks addressed by lanes 2b + i/8). P^T is the B operand straight from
+//    the QK accumulator registers: its token order fixes the order in which
+//    the transpose read gathers V.
+#include <mutex>
+#include <type_traits>
+
 #include "pda_internal.h"
 
 namespace pda {
+namespace {
 
-bool latent_supported(const pda_attn_shape& sh) {
-  (void)sh;
-  return false;
+constexpr int kDk = 576;            // latent key dims
+constexpr int kDv = 512;            // value dims (first 512 of the key)
+constexpr int kS = 64;              // page size
+constexpr int kGroups = kDk / 16;   // 16-dim column groups per token
+constexpr int kPageBytes = kDk * kS;
+constexpr int kHeadsPerWave = 32;
+constexpr int kMaxWaves = 4;
+constexpr int kThreadsL = 64 * kMaxWaves;
+static_assert((kDk * kS) / (16 * 64) % 4 == 0 && (kDk * kS) / (16 * 64) % 3 == 0,
+              "page copies must split evenly over 1..4 waves");
+constexpr float kTauL = 8.0f;
+constexpr float kLog2eL = 1.4426950408889634f;
+constexpr int kHdrL = 64;           // header ints, then pref[B+1]
+constexpr int kRow = kDv + 4;       // partial row: Dv sums, max, sum, 2 pad (16-byte rows)
+constexpr int kMaxSeqsL = 8192;
+
+template <int F, int L>
+struct sfor {
+  template <typename Fn>
+  __device__ __forceinline__ static void run(Fn&& fn) {
+    if constexpr (F < L) {
+      fn(std::integral_constant<int, F>{});
+      sfor<F + 1, L>::run(fn);
+    }
+  }
+};
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+
+struct LatArgs {
+  const uint16_t* __restrict__ q;
+  const uint8_t* __restrict__ kc;
+  const float* __restrict__ tscale;
+  const int32_t* __restrict__ bt;
+  const int32_t* __restrict__ lens;
+  const int32_t* __restrict__ verdict;
+  int32_t* hdr;         // [0] total pages T, [1] workgroups used, pref at kHdrL
+  float* part;          // slots x Hq x (Dv + 2)
+  float* out;
+  int B, Hq, P, max_blocks;
+  float sm_scale;
+};
+
+__device__ __forceinline__ int seq_pages(const LatArgs& a, int s) {
+  const int len = a.lens[s];
+  if (len <= 0 || len > a.max_blocks * kS) return 0;
+  if (a.verdict != nullptr && a.verdict[s] != 0) return 0;
+  return (len + kS - 1) / kS;
 }
 
+// Workgroup owning global page g when T pages are cut into W ranges
+// [floor(wT/W), floor((w+1)T/W)).
+__device__ __forceinline__ int owner_of(long long g, long long T, long long W) {
+  return (int)(((g + 1) * W - 1) / T);
+}
+
+// Per-page LDS staging: codes, then three per-token arrays.
+struct PageBuf {
+  uint8_t codes[kPageBytes];
+  float a[kS];     // scale * sm_scale * log2 e   (0 for tokens past the end)
+  float b[kS];     // log2(scale)                  (-inf past the end)
+  float inv[kS];   // 1 / scale                    (0 past the end)
+};
+
+// acc[d] *= alpha for the (rare) running-max move, through global memory:
+// store the accumulators (lane's head row, layout of the partial), wait, and
+// load them back scaled. The row belongs to this lane alone.
+__device__ __forceinline__ void rescale_via(float* row, f32x16_t (&acc)[kDv / 32], float alpha) {
+  const int h = __lane_id() >> 5;
+#pragma unroll
+  for (int d = 0; d < kDv / 32; ++d)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      *reinterpret_cast<float4*>(row + 32 * d + r4 * 8 + 4 * h) =
+          make_float4(acc[d][4 * r4], acc[d][4 * r4 + 1], acc[d][4 * r4 + 2], acc[d][4 * r4 + 3]);
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+  for (int d = 0; d < kDv / 32; ++d)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const float4 v = *reinterpret_cast<const float4*>(row + 32 * d + r4 * 8 + 4 * h);
+      acc[d][4 * r4] = v.x * alpha;
+      acc[d][4 * r4 + 1] = v.y * alpha;
+      acc[d][4 * r4 + 2] = v.z * alpha;
+      acc[d][4 * r4 + 3] = v.w * alpha;
+    }
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void latent_partial_kernel(LatArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  PageBuf* buf = reinterpret_cast<PageBuf*>(smem);                 // [2]
+  int* tmp = reinterpret_cast<int*>(smem + 2 * sizeof(PageBuf));   // kThreadsL + 1
+  int* pref = tmp + kThreadsL + 1;                                  // B + 1
+  constexpr int NT = 64 * NW;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;        // half-wave
+  const int n = lane & 31;        // head within the wave's 32 / MFMA column
+
+  // the prefix needs all kThreadsL slots of tmp; threads beyond NT count 0
+  const int T = [&] {
+    const int per = (a.B + NT - 1) / NT;
+    const int beg = min(a.B, tid * per);
+    const int end = min(a.B, beg + per);
+    int local = 0;
+    for (int s = beg; s < end; ++s) local += seq_pages(a, s);
+    tmp[tid] = local;
+    __syncthreads();
+    if (tid == 0) {
+      int run = 0;
+      for (int i = 0; i < NT; ++i) {
+        const int v = tmp[i];
+        tmp[i] = run;
+        run += v;
+      }
+      tmp[NT] = run;
+    }
+    __syncthreads();
+    int run = tmp[tid];
+    for (int s = beg; s < end; ++s) {
+      pref[s] = run;
+      run += seq_pages(a, s);
+    }
+    const int total = tmp[NT];
+    if (tid == 0) pref[a.B] = total;
+    __syncthreads();
+    return total;
+  }();
+  const long long W = min((long long)gridDim.x, (long long)T);
+  if (blockIdx.x == 0) {
+    for (int s = tid; s <= a.B; s += NT) a.hdr[kHdrL + s] = pref[s];
+    if (tid == 0) {
+      a.hdr[0] = T;
+      a.hdr[1] = (int)W;
+    }
+  }
+  if ((long long)blockIdx.x >= W) return;
+  const int w = blockIdx.x;
+  const int lo = (int)((long long)w * T / W);
+  const int hi = (int)((long long)(w + 1) * T / W);
+  const float c0 = a.sm_scale * kLog2eL;
+  const int head0 = wave * kHeadsPerWave;
+
+  int g = lo;
+  while (g < hi) {
+    // sequence owning global page g: last s with pref[s] <= g
+    int sl = 0, sh = a.B;
+    while (sh - sl > 1) {
+      const int mid = (sl + sh) >> 1;
+      if (pref[mid] <= g) sl = mid; else sh = mid;
+    }
+    const int s = __builtin_amdgcn_readfirstlane(sl);
+    const int j0 = g - pref[s];
+    const int j1 = min(hi, pref[s + 1]) - pref[s];
+    const int len = a.lens[s];
+    const int32_t* btrow = a.bt + (int64_t)s * a.max_blocks;
+    auto part_of = [&](int sq) {
+      return a.part + ((int64_t)(w + sq) * a.Hq + head0 + n) * kRow;
+    };
+
+    // ---- Q of this wave's heads, resident for the fragment --------------
+    // B operand of k-step k: lane (head n, half h) holds dims 16k + 8h .. +7.
+    bf16x8_t qreg[kGroups];
+    {
+      const uint16_t* qrow = a.q + ((int64_t)s * a.Hq + head0 + n) * kDk + 8 * h;
+#pragma unroll
+      for (int k = 0; k < kGroups; ++k)
+        qreg[k] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qrow + 16 * k));
+    }
+
+    f32x16_t acc[kDv / 32];
+#pragma unroll
+    for (int d = 0; d < kDv / 32; ++d) acc[d] = f32x16_t{};
+    float m = -INFINITY;   // running max of y for head n (same in both halves)
+    float l = 0.0f;        // this lane's tokens' share of the weight sum
+    bool bad = false;
+
+    // ---- page staging ------------------------------------------------------
+    // The page (36 column groups x 64 tokens x 16 bytes, contiguous) is
+    // copied global -> LDS directly (global_load_lds_dwordx4: each lane's 16
+    // bytes land at the wave-uniform LDS address + 16 * lane), so staging
+    // takes no registers. The copy of page j+1 runs while page j computes.
+    constexpr int kWaveChunks = kPageBytes / (16 * 64);    // 36 wave copies
+    float sc_next = 0.0f;
+    auto fetch = [&](int j, PageBuf& pb) {
+      int page = btrow[j];
+      if (page < 0 || page >= a.P) {
+        bad = true;
+        page = 0;
+      }
+      const uint8_t* src = a.kc + (int64_t)page * kPageBytes;
+#pragma unroll
+      for (int ii = 0; ii < kWaveChunks / NW; ++ii) {
+        const int i = ii * NW + wave;
+        __builtin_amdgcn_global_load_lds(
+            (const void __attribute__((address_space(1)))*)(src + (i * 64 + lane) * 16),
+            (void __attribute__((address_space(3)))*)(pb.codes + i * 1024), 16, 0, 0);
+      }
+      if (tid < kS) sc_next = a.tscale[(int64_t)page * kS + tid];
+    };
+    // After the copy of page j has landed: zero the codes of tokens past the
+    // end (they then add nothing, whatever the slot held) and fill the
+    // per-token arrays.
+    auto finish = [&](int j, PageBuf& pb) {
+      const int valid = min(kS, len - j * kS);   // tokens of this page in use
+      if (valid < kS) {
+        for (int c = tid; c < kPageBytes / 16; c += NT)
+          if ((c % kS) >= valid) *reinterpret_cast<uint4*>(pb.codes + c * 16) = make_uint4(0, 0, 0, 0);
+      }
+      if (tid < kS) {
+        // v_log_f32 is log2
+        const bool live = tid < valid;
+        pb.a[tid] = live ? sc_next * c0 : 0.0f;
+        pb.b[tid] = live ? __builtin_amdgcn_logf(sc_next) : -INFINITY;
+        pb.inv[tid] = live ? 1.0f / sc_next : 0.0f;
+      }
+    };
+
+    fetch(j0, buf[0]);
+    for (int j = j0; j < j1; ++j) {
+      PageBuf& pb = buf[(j - j0) & 1];
+      // page j's copy (and every earlier load) complete, then publish
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      finish(j, pb);
+      __syncthreads();
+      // the other buffer's last readers passed the barriers above
+      if (j + 1 < j1) fetch(j + 1, buf[(j + 1 - j0) & 1]);
+
+      // ---- QK: S^T (64 tokens x 32 heads) as two 32x32 tiles --------------
+      // A operand of k-step k, tile t: lane (token 32t + n, half h) holds the
+      // codes of dims 16k + 8h .. +7 (8 bytes, one LDS read). Reads run one
+      // step ahead; the scheduling barrier per step keeps the compiler from
+      // hoisting every read and conversion (a register each).
+      f32x16_t st[2] = {f32x16_t{}, f32x16_t{}};
+      {
+        const uint8_t* rowp = pb.codes + n * 16 + 8 * h;
+        uint2 cur0 = *reinterpret_cast<const uint2*>(rowp);
+        uint2 cur1 = *reinterpret_cast<const uint2*>(rowp + 32 * 16);
+        sfor<0, kGroups>::run([&](auto K) {
+          constexpr int k = decltype(K)::value;
+          uint2 nx0 = cur0, nx1 = cur1;
+          if constexpr (k + 1 < kGroups) {
+            nx0 = *reinterpret_cast<const uint2*>(rowp + (k + 1) * (kS * 16));
+            nx1 = *reinterpret_cast<const uint2*>(rowp + (k + 1) * (kS * 16) + 32 * 16);
+          }
+          {
+            const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur0.x, 1.0f, false);
+            const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur0.x, 1.0f, true);
+            const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur0.y, 1.0f, false);
+            const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur0.y, 1.0f, true);
+            const bf16x8_t av = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+            st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[k], st[0], 0, 0, 0);
+          }
+          {
+            const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur1.x, 1.0f, false);
+            const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur1.x, 1.0f, true);
+            const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur1.y, 1.0f, false);
+            const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur1.y, 1.0f, true);
+            const bf16x8_t av = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+            st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[k], st[1], 0, 0, 0);
+          }
+          cur0 = nx0;
+          cur1 = nx1;
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
+
+      // ---- softmax (log2 units, scale folded in) --------------------------
+      // register r of tile t holds token 32t + (r/4)*8 + 4h + r%4
+      float bm = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int t0 = 32 * t + r4 * 8 + 4 * h;
+          const float4 av = *reinterpret_cast<const float4*>(pb.a + t0);
+          const float4 bv = *reinterpret_cast<const float4*>(pb.b + t0);
+          const float aa[4] = {av.x, av.y, av.z, av.w};
+          const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = fmaf(st[t][4 * r4 + i], aa[i], bb[i]);
+            st[t][4 * r4 + i] = v;
+            bm = fmaxf(bm, v);
+          }
+        }
+      }
+      bm = fmaxf(bm, shfl_xor_f32(bm, 32));
+      if (__ballot(bm > m + kTauL) != 0) {
+        // some head's max moved by more than the threshold: rescale those
+        const bool mv = bm > m + kTauL;
+        const float mn = mv ? bm : m;
+        if (m != -INFINITY) {   // uniform: every head has a finite max after page 1
+          const float alpha = mv ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
+          l *= alpha;
+          // acc *= alpha, as a round trip through this fragment's partial
+          // slot (written again at the end): multiplying the accumulators in
+          // place would pull all of them out of the matrix-core registers
+          rescale_via(part_of(s), acc, alpha);
+        }
+        m = mn;
+      }
+      // p' = 2^(y - m), packed to f16 as the B operand of PV: k-step
+      // ks = 2t + s2 takes registers 8*s2 .. 8*s2+7 of tile t
+      f16x8_t pk[4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int t0 = 32 * t + r4 * 8 + 4 * h;
+          const float4 iv = *reinterpret_cast<const float4*>(pb.inv + t0);
+          const float ii[4] = {iv.x, iv.y, iv.z, iv.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = __builtin_amdgcn_exp2f(st[t][4 * r4 + i] - m);
+            l = fmaf(p, ii[i], l);
+            pk[2 * t + r4 / 2][4 * (r4 & 1) + i] = (_Float16)p;
+          }
+        }
+      }
+
+      // ---- PV: O^T (512 dims x 32 heads) += V^T P^T ------------------------
+      // k-step ks = 2t + s2: row b of the transpose read is token
+      // 16ks + (b/4)*8 + 4hh + b%4 where hh is the half-wave of the receiving
+      // lanes (lanes 0-31 receive k = 0..7, lanes 32-63 k = 8..15). In 16-lane
+      // group gq (hh = gq/2, dims 16*(gq%2) + 0..15 of the tile), lane 2b + e
+      // supplies token row b, bytes 8e..8e+7 of its 16 dims.
+      {
+        const int gq = lane >> 4;
+        const int hh = gq >> 1;
+        const int li = lane & 15;
+        const int bb = li >> 1;
+        const int e = li & 1;
+        const uint8_t* vbase = pb.codes + ((bb >> 2) * 8 + 4 * hh + (bb & 3)) * 16 + 8 * e +
+                               (gq & 1) * (kS * 16);
+        auto rd = [&](int ks, int d) -> i32x2_t {
+          return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) i32x2_t*)(vbase + 16 * ks * 16 +
+                                                           2 * d * (kS * 16)));
+        };
+        i32x2_t cw = rd(0, 0);
+        sfor<0, 4 * (kDv / 32)>::run([&](auto I) {
+          constexpr int ks = decltype(I)::value / (kDv / 32);
+          constexpr int d = decltype(I)::value % (kDv / 32);
+          i32x2_t nx = cw;
+          if constexpr (d + 1 < kDv / 32) nx = rd(ks, d + 1);
+          else if constexpr (ks + 1 < 4) nx = rd(ks + 1, 0);
+          const f16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)cw.x, 1.0f, false);
+          const f16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)cw.x, 1.0f, true);
+          const f16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)cw.y, 1.0f, false);
+          const f16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)cw.y, 1.0f, true);
+          const f16x8_t av = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y, v3.x, v3.y};
+          acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pk[ks], acc[d], 0, 0, 0);
+          cw = nx;
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
+    }
+
+    // ---- partial of this fragment -------------------------------------------
+    float* part = part_of(s);
+    const float lt = l + shfl_xor_f32(l, 32);
+    const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
+    if (any_bad) {
+      if (h == 0) part[kDv] = __builtin_nanf("");
+    } else {
+      // acc[d] register r: dim 32d + (r/4)*8 + 4h + r%4 of head n
+#pragma unroll
+      for (int d = 0; d < kDv / 32; ++d) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          float4 v = make_float4(acc[d][4 * r4], acc[d][4 * r4 + 1], acc[d][4 * r4 + 2],
+                                 acc[d][4 * r4 + 3]);
+          *reinterpret_cast<float4*>(part + 32 * d + r4 * 8 + 4 * h) = v;
+        }
+      }
+      if (h == 0) {
+        part[kDv] = m;
+        part[kDv + 1] = lt;
+      }
+    }
+    g = pref[s] + j1;
+    __syncthreads();
+  }
+}
+
+// Merge the fragments of one sequence: one workgroup per (sequence, 4 heads),
+// 64 threads per head, 8 dims per thread.
+__global__ __launch_bounds__(256) void latent_combine_kernel(LatArgs a) {
+  const int s = blockIdx.x / (a.Hq / 4);
+  const int hd = (blockIdx.x % (a.Hq / 4)) * 4 + (threadIdx.x >> 6);
+  const int d0 = (threadIdx.x & 63) * 8;
+  float* o = a.out + ((int64_t)s * a.Hq + hd) * kDv + d0;
+  const int len = a.lens[s];
+  const bool aborted = a.verdict != nullptr && a.verdict[s] != 0;
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (aborted || len == 0) {
+    reinterpret_cast<float4*>(o)[0] = z4;
+    reinterpret_cast<float4*>(o)[1] = z4;
+    return;
+  }
+  const float qnan = __builtin_nanf("");
+  const float4 n4 = make_float4(qnan, qnan, qnan, qnan);
+  if (len < 0 || len > a.max_blocks * kS) {
+    reinterpret_cast<float4*>(o)[0] = n4;
+    reinterpret_cast<float4*>(o)[1] = n4;
+    return;
+  }
+  const long long T = a.hdr[0];
+  const long long W = a.hdr[1];
+  const int* pref = a.hdr + kHdrL;
+  const int w0 = owner_of(pref[s], T, W);
+  const int w1 = owner_of(pref[s + 1] - 1, T, W);
+  float M = -INFINITY;
+  bool nan = false;
+  for (int w = w0; w <= w1; ++w) {
+    const float mw = a.part[((int64_t)(w + s) * a.Hq + hd) * kRow + kDv];
+    nan |= __builtin_isnan(mw);
+    M = fmaxf(M, mw);
+  }
+  if (nan) {
+    reinterpret_cast<float4*>(o)[0] = n4;
+    reinterpret_cast<float4*>(o)[1] = n4;
+    return;
+  }
+  float L = 0.0f;
+  float4 x0 = z4, x1 = z4;
+  for (int w = w0; w <= w1; ++w) {
+    const float* pw = a.part + ((int64_t)(w + s) * a.Hq + hd) * kRow;
+    const float f = __builtin_amdgcn_exp2f(pw[kDv] - M);
+    L += f * pw[kDv + 1];
+    const float4 v0 = reinterpret_cast<const float4*>(pw + d0)[0];
+    const float4 v1 = reinterpret_cast<const float4*>(pw + d0)[1];
+    x0.x += f * v0.x; x0.y += f * v0.y; x0.z += f * v0.z; x0.w += f * v0.w;
+    x1.x += f * v1.x; x1.y += f * v1.y; x1.z += f * v1.z; x1.w += f * v1.w;
+  }
+  const float inv = 1.0f / L;
+  reinterpret_cast<float4*>(o)[0] = make_float4(x0.x * inv, x0.y * inv, x0.z * inv, x0.w * inv);
+  reinterpret_cast<float4*>(o)[1] = make_float4(x1.x * inv, x1.y * inv, x1.z * inv, x1.w * inv);
+}
+
+size_t lat_header_bytes(int B) {
+  const size_t h = (size_t)(kHdrL + B + 1) * sizeof(int32_t);
+  return (size_t)((h + 255) & ~(size_t)255);
+}
+
+size_t lat_slot_bytes(const pda_attn_shape& sh) {
+  return (size_t)sh.num_q_heads * kRow * sizeof(float);
+}
+
+size_t lat_lds_bytes(int B) {
+  return 2 * sizeof(PageBuf) + (size_t)(kThreadsL + 1 + B + 1) * sizeof(int);
+}
+
+typedef void (*lat_kernel_t)(LatArgs);
+
+lat_kernel_t pick_latent(int nw) {
+  switch (nw) {
+    case 1: return latent_partial_kernel<1>;
+    case 2: return latent_partial_kernel<2>;
+    case 3: return latent_partial_kernel<3>;
+    default: return latent_partial_kernel<4>;
+  }
+}
+
+}  // namespace
+
+int device_cu_count();
+
+bool latent_supported(const pda_attn_shape& sh) {
+  return sh.v_in_k == 1 && sh.kv_dtype == PDA_KV_FP8_E4M3 &&
+         sh.scale_mode == PDA_SCALE_PER_TOKEN && sh.num_kv_heads == 1 &&
+         sh.head_dim_qk == kDk && sh.head_dim_v == kDv && sh.page_size == kS &&
+         sh.num_q_heads % kHeadsPerWave == 0 && sh.num_q_heads <= kHeadsPerWave * kMaxWaves &&
+         sh.num_seqs <= kMaxSeqsL;
+}
+
+// One workgroup per compute unit; every workgroup may leave one partial per
+// sequence fragment, and slot (workgroup + sequence) is unique.
 size_t latent_workspace_bytes(const pda_attn_shape& sh, int32_t max_seq_len) {
-  (void)sh;
   (void)max_seq_len;
-  return 0;
+  const size_t slots = (size_t)device_cu_count() + (size_t)sh.num_seqs;
+  return lat_header_bytes(sh.num_seqs) + slots * lat_slot_bytes(sh);
 }
 
 int latent_launch(const pda_attn_shape& sh, const void* q, const void* k_cache,
                   const float* token_scale, const int32_t* block_table, const int32_t* seq_lens,
                   int32_t max_seq_len, const int32_t* verdict, void* workspace,
                   size_t workspace_bytes, float* out, hipStream_t stream) {
-  (void)sh; (void)q; (void)k_cache; (void)token_scale; (void)block_table; (void)seq_lens;
-  (void)max_seq_len; (void)verdict; (void)workspace; (void)workspace_bytes; (void)out;
-  (void)stream;
-  return PDA_ERR_UNSUPPORTED;
+  (void)max_seq_len;
+  const size_t hdr = lat_header_bytes(sh.num_seqs);
+  const size_t slot = lat_slot_bytes(sh);
+  if (workspace_bytes < hdr + slot * ((size_t)sh.num_seqs + 1)) return PDA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return PDA_ERR_INVALID_ARG;
+  long long grid = device_cu_count();
+  const long long fit = (long long)((workspace_bytes - hdr) / slot) - sh.num_seqs;
+  if (grid > fit) grid = fit;
+  if (grid < 1) grid = 1;
+  LatArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kc = static_cast<const uint8_t*>(k_cache);
+  a.tscale = token_scale;
+  a.bt = block_table;
+  a.lens = seq_lens;
+  a.verdict = verdict;
+  a.hdr = static_cast<int32_t*>(workspace);
+  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + hdr);
+  a.out = out;
+  a.B = sh.num_seqs;
+  a.Hq = sh.num_q_heads;
+  a.P = sh.num_pages;
+  a.max_blocks = sh.max_blocks_per_seq;
+  a.sm_scale = sh.sm_scale;
+  const int nw = sh.num_q_heads / kHeadsPerWave;
+  const size_t lds = lat_lds_bytes(sh.num_seqs);
+  lat_kernel_t k = pick_latent(nw);
+  static std::once_flag once[kMaxWaves];
+  bool attr_ok = true;
+  std::call_once(once[nw - 1], [&] {
+    attr_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lat_lds_bytes(kMaxSeqsL)) == hipSuccess;
+  });
+  if (!attr_ok) return PDA_ERR_LAUNCH;
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(64 * nw), lds, stream, a);
+  if (hipGetLastError() != hipSuccess) return PDA_ERR_LAUNCH;
+  hipLaunchKernelGGL(latent_combine_kernel, dim3((unsigned)(sh.num_seqs * (sh.num_q_heads / 4))),
+                     dim3(256), 0, stream, a);
+  return launch_status();
 }
 
 }  // namespace pda

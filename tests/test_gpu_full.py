@@ -84,3 +84,17 @@ def test_workload5_sampled(gpu):
     mx, rel = assert_attn_close(got, ref, "workload 5")
     log(f"  workload 5: max_abs {mx:.3e} rel_l2 {rel:.3e}")
     assert np.all(got[[samples.index(inj[0])]] == 0)
+
+
+def test_workload4_sampled(gpu):
+    """Latent workload (64 sequences of U[1024, 32768] tokens, 128 query
+    heads, one 576-dim kv head, pages of 64, per-token scales) on the MFMA
+    path; the shortest, the longest and a random sequence are compared."""
+    log("workload 4 full size")
+    b0 = synth.make_batch(4)
+    lens = b0.seq_lens
+    samples = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 17})
+    b, verdict, got, ref, _ = _run(gpu, 4, synth.KV_FP8, samples)
+    assert np.all(verdict == 0)
+    mx, rel = assert_attn_close(got, ref, "workload 4")
+    log(f"  workload 4: max_abs {mx:.3e} rel_l2 {rel:.3e}")
