@@ -217,6 +217,33 @@ __device__ __forceinline__ void load_k(const AttnArgs& a, int g, const Pages& pg
   }
 }
 
+// FP8 keys of one 64-token block straight into the wave's LDS buffer
+// (global_load_lds_dwordx4: lane i's 16 bytes land at the wave-uniform LDS
+// address + 16 i), laid out [column group c][token][16 codes]: one 1 KB copy
+// per column group, and a token's 16 codes at kw + c*1024 + 16*token, so the
+// QK reads (lane = token) are conflict-free. No registers hold keys in flight.
+template <int S>
+__device__ __forceinline__ void dma_k(const AttnArgs& a, int g, const Pages& pg, uint8_t* kw) {
+  const int lane = __lane_id();
+  int page = pg.p0;
+  if constexpr (S <= 32) page += (lane >= S) * (pg.p1 - pg.p0);
+  if constexpr (S == 16) page += (lane >= 2 * S) * (pg.p2 - pg.p1) + (lane >= 3 * S) * (pg.p3 - pg.p2);
+  const int off = lane % S;
+  const uint8_t* src = a.kc + ((((int64_t)page * a.Hkv + g) * 8) * S + off) * 16;
+  // Issued as inline asm so that the compiler's wait-count bookkeeping does
+  // not treat every later LDS read as dependent on it (it would wait for all
+  // vector-memory operations, including the next block's V loads); the one
+  // reader, the QK of the next block, waits for it explicitly.
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)kw));
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint8_t* gp = src + (int64_t)c * S * 16;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(lds0 + c * 1024), "v"(gp) : "memory");
+  }
+}
+
 // V of one 64-token block for the lane's two dims (2*lane, 2*lane+1): one
 // word per token pair. In the V format the pair row (page, g, off/2) holds
 // (dim d, token off) at element 2*d + off%2, so dims 2l and 2l+1 of both
@@ -241,7 +268,7 @@ __device__ __forceinline__ void load_v(const AttnArgs& a, int g, const Pages& pg
 // Step k = (ic, r) takes row r's four p pairs of token pairs 4ic..4ic+3 in
 // one 16-byte LDS read (a wave-uniform address, so a broadcast). Reads run
 // kPD steps ahead of their use.
-constexpr int kPD = 4;
+constexpr int kPD = 2;
 
 __device__ __forceinline__ uint32_t word0(uint32_t w) { return w; }
 __device__ __forceinline__ uint32_t word0(uint2 w) { return w.x; }
@@ -326,7 +353,7 @@ __device__ __forceinline__ void pv_block(
 
 template <int G, bool FP8, int S>
 __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, long long item,
-                             uint16_t* pw) {
+                             uint16_t* pw, uint8_t* kw) {
   using I = Item<G, FP8, S>;
   using W = typename I::vword_t;
   constexpr int NP = I::NP;
@@ -373,12 +400,16 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
     }
   };
 
-  uint4 kk[I::KQ];
+  // FP8 keys go through the wave's LDS buffer; BF16 keys through registers
+  uint4 kk[FP8 ? 1 : I::KQ];
   W vv[32];
   Pages pg;
   int b0 = tok0;
   pages_of(b0, pg);
-  load_k<G, FP8, S>(a, g, pg, kk);
+  if constexpr (FP8)
+    dma_k<S>(a, g, pg, kw);
+  else
+    load_k<G, FP8, S>(a, g, pg, kk);
   load_v<G, FP8, S>(a, g, pg, vv);
 
   for (;;) {
@@ -389,12 +420,52 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
     if (has_next) pages_of(bn, npg);
 
     // ---- QK: lane = token b0 + lane ------------------------------------
-    // Eight dims (four q pairs per row) at a time, q in SGPRs. The loads of
-    // chunk c+2 are released by a fence that consumes the scores produced by
-    // chunk c, so exactly two 4-pair chunks of q are live at any time.
     float z[G];
 #pragma unroll
     for (int r = 0; r < G; ++r) z[r] = 0.0f;
+    if constexpr (FP8) {
+      // Keys from the wave's LDS buffer, 16 dims (one 16-byte read) at a
+      // time; q from SGPRs, one 8-dword scalar load per (16 dims, row),
+      // issued two steps ahead (a ring of three). The fence ties each load
+      // to the scores computed so far, so loads cannot be hoisted early.
+      // The key copy of this block (the oldest vector-memory operations in
+      // flight; the 32 V loads of this block came before it and the next
+      // block's V loads are not issued yet) must have landed.
+      __builtin_amdgcn_s_waitcnt(0x8F70);   // vmcnt(32): all but the 32 V loads
+      uint32_t qb[3][8];
+      auto loadq = [&](int k, uint32_t(&dst)[8]) {
+        cu32_t* qp = fence_ptr_after<G>(qbase, z);
+        const int c16 = k / G, r = k % G;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dst[j] = qp[r * 64 + c16 * 8 + j];
+      };
+      loadq(0, qb[0]);
+      if constexpr (8 * G > 1) loadq(1, qb[1]);
+      bf16x2_t kp[8];
+      static_for<0, 8 * G>::run([&](auto K) {
+        constexpr int k = decltype(K)::value;
+        constexpr int c16 = k / G, r = k % G;
+        if constexpr (r == 0) {
+          const uint4 w = *reinterpret_cast<const uint4*>(kw + c16 * 1024 + lane * 16);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            kp[2 * j] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u4_get(w, j), 1.0f, false);
+            kp[2 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u4_get(w, j), 1.0f, true);
+          }
+        }
+        if constexpr (k + 2 < 8 * G) loadq(k + 2, qb[(k + 2) % 3]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          z[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qb[k % 3][j]),
+                                                 kp[j], z[r], false);
+        if constexpr (r == G - 1) __builtin_amdgcn_sched_barrier(0);
+      });
+      // every key read of this block has been consumed: the buffer is free
+      if (has_next) dma_k<S>(a, g, npg, kw);
+    } else {
+    // Eight dims (four q pairs per row) at a time, q in SGPRs. The loads of
+    // chunk c+2 are released by a fence that consumes the scores produced by
+    // chunk c, so exactly two 4-pair chunks of q are live at any time.
     {
       uint32_t qbuf[2][G][2];
       auto loadq = [&](int c4, uint32_t(&dst)[G][2]) {
@@ -436,6 +507,8 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
     }
     // K registers are free: prefetch the next block's keys.
     if (has_next) load_k<G, FP8, S>(a, g, npg, kk);
+    }
+
 
     // ---- online softmax (log2 units) -----------------------------------
     // zl = z*kmul - m. The running max m only moves when some score of the
@@ -526,7 +599,7 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
 // Waves per SIMD the register allocator must leave room for.
 template <int G, bool FP8>
 constexpr int partial_waves() {
-  return FP8 ? 3 : 2;
+  return FP8 ? 4 : 2;
 }
 
 template <int G, bool FP8, int S>
@@ -536,8 +609,10 @@ void attn_partial_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) int lds[];
   constexpr int PB = pbuf_bytes<G, FP8>();
   const int wave = threadIdx.x >> 6;
+  constexpr int KB = FP8 ? 8192 : 0;   // per-wave key buffer (FP8)
   uint16_t* pw = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(lds) + wave * PB);
-  int* tmp = lds + kWaves * PB / 4;   // kThreads + 1
+  uint8_t* kw = reinterpret_cast<uint8_t*>(lds) + kWaves * PB + wave * KB;
+  int* tmp = lds + kWaves * (PB + KB) / 4;   // kThreads + 1
   int* pref = tmp + kThreads + 1;     // B + 1
   int chunk;
   const int total_sc = build_plan(a, S, pref, tmp, chunk);
@@ -554,7 +629,7 @@ void attn_partial_kernel(AttnArgs a) {
     }
     const int s = __builtin_amdgcn_readfirstlane(lo);
     const int c = __builtin_amdgcn_readfirstlane(sc - pref[lo]);
-    process_item<G, FP8, S>(a, s, c, __builtin_amdgcn_readfirstlane(g), chunk, item, pw);
+    process_item<G, FP8, S>(a, s, c, __builtin_amdgcn_readfirstlane(g), chunk, item, pw, kw);
   }
 }
 
@@ -812,7 +887,8 @@ extern "C" int paged_decode_attn(const pda_attn_shape* shape, const void* q, con
 
   const kernel_t pk = fp8 ? pick_partial<true>(G, sh.page_size) : pick_partial<false>(G, sh.page_size);
   const combine_t ck = fp8 ? pick_combine<true>(G) : pick_combine<false>(G);
-  const size_t pbuf = (size_t)kWaves * (size_t)(fp8 ? 1 : 2) * (size_t)G * 64 * 2;
+  const size_t pbuf = (size_t)kWaves * ((size_t)(fp8 ? 1 : 2) * (size_t)G * 64 * 2 +
+                                          (fp8 ? 8192 : 0));
   const size_t lds = pbuf + (size_t)(kThreads + 1 + sh.num_seqs + 1) * sizeof(int);
   const long long ml = max_seq_len > 0 ? max_seq_len : 1;
   const long long items_bound = (long long)sh.num_seqs * sh.num_kv_heads * ((ml + chunk - 1) / chunk);

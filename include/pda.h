@@ -180,12 +180,15 @@ int validate_page_tags(const uint32_t* page_tags, int32_t num_pages,
 /*
  * paged_decode_attn_workspace_bytes — device scratch needed by
  * paged_decode_attn for `shape` when no sequence is longer than
- * max_seq_len tokens: a header plus one split-K partial (G rows of Dv fp32
- * accumulators, a running max and a running sum per row) per
- * (sequence, chunk, kv head). Returns 0 for an invalid shape.
- * A smaller workspace down to the size for max_seq_len = 1 is still
- * accepted; the device then widens the split chunk (by doubling) until the
- * partials fit, which changes results only within rounding.
+ * max_seq_len tokens. Vector-ALU path: a header plus one split-K partial
+ * (G rows of Dv fp32 accumulators, a running max and a running sum per row)
+ * per (sequence, chunk, kv head); a smaller workspace down to the size for
+ * max_seq_len = 1 is still accepted, and the device then widens the split
+ * chunk (by doubling) until the partials fit, which changes results only
+ * within rounding. Latent path: a header plus one partial (Hq rows of Dv + 4
+ * fp32) per (compute unit + sequence) of the current device; with less room
+ * fewer workgroups are launched (at least one partial per sequence plus one
+ * is required). Returns 0 for an invalid shape.
  */
 size_t paged_decode_attn_workspace_bytes(const pda_attn_shape* shape,
                                          int32_t max_seq_len);
@@ -225,8 +228,12 @@ size_t paged_decode_attn_workspace_bytes(const pda_attn_shape* shape,
  *               its first ceil(len/S) entries, are NaN (no out-of-range
  *               address is ever formed).
  *  Supported: FP8 or BF16, PER_HEAD/NONE, Dk == Dv == 128, Hq/Hkv in
- *  {1,2,4,8}, S in {16, 32, 64}; and latent FP8 PER_TOKEN, Hkv == 1,
- *  Dk == 576, Dv == 512, v_in_k, S == 64, Hq a multiple of 16.
+ *  {1,2,4,8}, S in {16, 32, 64}, num_seqs <= 16384 (vector-ALU kernel);
+ *  and latent FP8 PER_TOKEN, Hkv == 1, Dk == 576, Dv == 512, v_in_k,
+ *  S == 64, Hq in {32, 64, 96, 128}, num_seqs <= 8192 (matrix-core kernel;
+ *  split_tokens is ignored there: the valid pages of all sequences are cut
+ *  into one equal range per compute unit, and the workspace holds one
+ *  partial per (range, sequence) pair that meets).
  */
 int paged_decode_attn(const pda_attn_shape* shape, const void* q,
                       const void* k_cache, const void* v_cache,
