@@ -30,7 +30,29 @@ if ROOT not in sys.path:
 
 METRIC = ("decode-attn KV GB/s (% HBM peak) + seq-steps/s, FP8 vs BF16 KV, 64×8k ctx")
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD specification
+MFMA_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 / f16 matrix peak, AMD specification
 WORKLOAD_ID = 3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_64x8k.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_fp8_write_amd", "csrc", "decode_attn.hip")
+
+
+def measured_traffic():
+    """HBM bytes per attention call (partial + combine) from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled by the copy-kernel
+    calibration; None when the kernel source changed since they were taken."""
+    import hashlib
+    try:
+        fields = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        if fields.get("decode_attn.hip sha256") != sha:
+            return None
+        return int(fields["hbm bytes per attention call"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def log(msg):
@@ -114,6 +136,49 @@ def cpu_baseline(batch, data, host_scales, target_s=12.0):
                       f"attention; {t:.1f} s"}
 
 
+def other_workload(args, torch, np, synth, pda, workload):
+    """One FP8 line for workload 2, 4 (latent, matrix-core path) or 5 (full
+    pool with tag mismatches), timed like the metric's workload."""
+    batch = synth.make_batch(args.workload)
+    cfg = batch.cfg
+    log(f"workload {args.workload}: generating inputs")
+    data = synth.map_seqs(lambda s: batch.kv(s), list(range(batch.B)),
+                          min(16, os.cpu_count() or 1))
+    db = workload.build(batch, pda.KV_FP8_E4M3, data=data)
+    db.alloc_workspace()
+    del data
+    r = time_steps(db, args.steps, args.warmup, torch)
+    kv = workload.kv_bytes(batch, pda.KV_FP8_E4M3)
+    attn_s = r["attn_ms"] * 1e-3
+    step_s = r["step_ms"] * 1e-3
+    flops = workload.attention_flops(batch)
+    line = {
+        "metric": f"decode-attn KV GB/s, FP8 KV, workload {args.workload}",
+        "value": kv / step_s / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": r["step_ms"], "higher_is_better": True,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "global_batch": batch.B,
+                   "tokens": int(batch.seq_lens.sum())},
+        "attn_ms": r["attn_ms"], "validate_ms": r["validate_ms"],
+        "kv_write_ms": r["kv_write_ms"], "seq_steps_per_s": batch.B / step_s,
+        "kv_GBps_attn": kv / attn_s / 1e9,
+        "verdicts_nonzero": int((db.verdict.cpu().numpy() != 0).sum()),
+    }
+    if cfg.v_in_k:
+        tf = flops / attn_s / 1e12
+        line["roofline"] = {"kernel": "paged_decode_attn latent (partial + combine)",
+                            "bound": "mfma", "achieved": tf, "peak": MFMA_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": tf / MFMA_PEAK_TFLOPS,
+                            "hbm_frac": kv / attn_s / 1e9 / HBM_PEAK_GBPS,
+                            "algorithmic_flops_per_launch": flops, "traffic": None}
+    else:
+        line["roofline"] = {"kernel": "paged_decode_attn (attn_partial + attn_combine)",
+                            "bound": "hbm", "achieved": kv / attn_s / 1e9,
+                            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": kv / attn_s / 1e9 / HBM_PEAK_GBPS, "traffic": None}
+    return line
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +186,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--workload", type=int, default=WORKLOAD_ID, choices=(2, 3, 4, 5),
+                    help="3 (default) is the metric's workload; 2, 4 and 5 print an extra "
+                         "line for the other full-size workloads (4 = latent, matrix cores)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy, whose HBM "
                          "counters calibrate FETCH_SIZE / WRITE_SIZE in a profiled run")
@@ -150,6 +218,9 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
         log("copy calibration: 1 GiB read + 1 GiB written by one copy kernel")
+    if args.workload != WORKLOAD_ID:
+        print(json.dumps(other_workload(args, torch, np, synth, pda, workload)), flush=True)
+        return
     batch = synth.make_batch(WORKLOAD_ID)
     cfg = batch.cfg
     log("generating inputs")
@@ -218,7 +289,8 @@ def main():
         "roofline": {"kernel": "paged_decode_attn (attn_partial + attn_combine)",
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "algorithmic_bytes_per_launch": attn_bytes, "traffic": None},
+                     "algorithmic_bytes_per_launch": attn_bytes,
+                     "traffic": measured_traffic()},
     }
     if res_bf16 is not None:
         line["bf16"] = res_bf16

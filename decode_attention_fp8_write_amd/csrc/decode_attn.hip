@@ -18,23 +18,25 @@
 // running max, running sum) go to the workspace; the combine kernel merges
 // them with a log-sum-exp rule.
 //
-// Inside an item a wave walks 64 tokens at a time (four 16-token lane groups):
-//  * QK: lane = token. The lane loads its token's 128 K codes (16-byte
-//    column groups of the K format, contiguous across the 16 lanes of a
-//    group), converts pairs of codes to bf16 exactly, and accumulates
-//    q·k for all G query rows with v_dot2c_f32_bf16 whose q operand is a
-//    wave-uniform value held in SGPRs.
-//  * softmax: scores in log2 units; wave max per row through DPP; the
-//    running max is only moved when the block max exceeds it by more than
-//    TAU (then p <= 2^TAU), so rescaling the accumulators is rare.
-//  * PV: lane = (16-token group, 8 dims). V pairs of adjacent tokens are
-//    interleaved in the V format, so one converted dword is an f16 pair along
-//    the token axis; p pairs are packed once per block and broadcast inside
-//    the 16-lane group with DPP row_newbcast; v_dot2c_f32_f16 accumulates
-//    G x 8 outputs per lane. BF16 caches use bf16 dots with p split into a
-//    bf16 high part and a bf16 remainder (relative error 2^-16).
-// Every dot accumulates in fp32; q enters exactly (bf16), K and V codes
-// convert exactly, and p is rounded once (f16 nearest-even, or hi+lo bf16).
+// Inside an item a wave walks 64 tokens (a block) at a time:
+//  * QK: lane = token. FP8 keys reach the wave's own LDS buffer by direct
+//    global->LDS copies issued one block ahead (no registers hold them in
+//    flight); BF16 keys come through registers. Code pairs convert exactly to
+//    bf16 and v_dot2_f32_bf16 accumulates q.k for all G query rows, the q
+//    operand a wave-uniform SGPR pair fetched by scalar loads.
+//  * softmax in log2 units with a lazy running max: it only moves when some
+//    score of the block exceeds it by more than kTau (a per-row ballot), so
+//    p <= 2^kTau and the wave-wide maximum is rarely needed.
+//  * p goes to the wave's LDS buffer (f16, or a bf16 high part and a bf16
+//    remainder for BF16 caches, relative error 2^-16).
+//  * PV: lane = two dims, all 64 tokens. The V format puts the two tokens of
+//    an even/odd slot pair next to each other, so one V word is (dim, 2
+//    tokens) x 2 dims; its codes convert exactly to two f16 pairs and
+//    v_dot2_f32_f16 takes the matching p pair, read from LDS as a broadcast
+//    (one 16-byte read gives a row's four p pairs).
+//  * V of the next block is loaded into registers once PV is done.
+// Every dot product accumulates in fp32; q enters exactly (bf16), K and V
+// codes convert exactly, and p is rounded once.
 #include <mutex>
 #include <type_traits>
 
@@ -657,12 +659,22 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a, int 
   const int* pref = a.ws_hdr + kHdrInts;
   const int c0 = pref[s], c1 = pref[s + 1];
   const int64_t stride = G * (kD + 2);
+  // chunks are read eight at a time so that eight loads are in flight; the
+  // merge order is the chunk order, so the result is deterministic
+  constexpr int kB = 8;
   float M = -INFINITY;
   bool nan = false;
-  for (int c = c0; c < c1; ++c) {
-    const float mc = a.ws_part[((int64_t)c * a.Hkv + g) * stride + G * kD + r];
-    nan |= __builtin_isnan(mc);
-    M = fmaxf(M, mc);
+  for (int c = c0; c < c1; c += kB) {
+    float mc[kB];
+#pragma unroll
+    for (int i = 0; i < kB; ++i)
+      mc[i] = (c + i < c1) ? a.ws_part[((int64_t)(c + i) * a.Hkv + g) * stride + G * kD + r]
+                           : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      nan |= __builtin_isnan(mc[i]);
+      M = fmaxf(M, mc[i]);
+    }
   }
   if (nan) {
     *reinterpret_cast<float4*>(o) = make_float4(qnan, qnan, qnan, qnan);
@@ -670,15 +682,31 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a, int 
   }
   float L = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c = c0; c < c1; ++c) {
-    const float* pc = a.ws_part + ((int64_t)c * a.Hkv + g) * stride;
-    const float w = exp2f(pc[G * kD + r] - M);
-    L += w * pc[G * kD + G + r];
-    const float4 v = *reinterpret_cast<const float4*>(pc + r * kD + d4);
-    acc.x += w * v.x;
-    acc.y += w * v.y;
-    acc.z += w * v.z;
-    acc.w += w * v.w;
+  for (int c = c0; c < c1; c += kB) {
+    float mc[kB], lc[kB];
+    float4 v[kB];
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      if (c + i < c1) {
+        const float* pc = a.ws_part + ((int64_t)(c + i) * a.Hkv + g) * stride;
+        mc[i] = pc[G * kD + r];
+        lc[i] = pc[G * kD + G + r];
+        v[i] = *reinterpret_cast<const float4*>(pc + r * kD + d4);
+      } else {
+        mc[i] = -INFINITY;
+        lc[i] = 0.0f;
+        v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      const float w = __builtin_amdgcn_exp2f(mc[i] - M);
+      L += w * lc[i];
+      acc.x += w * v[i].x;
+      acc.y += w * v[i].y;
+      acc.z += w * v[i].z;
+      acc.w += w * v[i].w;
+    }
   }
   const float f = (FP8 ? a.v_scale[g] : 1.0f) / L;
   *reinterpret_cast<float4*>(o) = make_float4(acc.x * f, acc.y * f, acc.z * f, acc.w * f);

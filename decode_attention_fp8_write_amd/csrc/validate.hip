@@ -14,10 +14,16 @@
 // "Cloudflare Workers AI: Kimi および GLM の推論を大規模に最適化する", section
 // "KV キャッシュ整合性チェック").
 //
-// One wave per sequence walks its logical blocks 64 at a time (coalesced
-// block-table and expected-tag reads, a gather of the current tags) and stops
-// at the first window holding a failing block; the lowest failing index is a
-// ballot + find-first-set, so the verdict is deterministic.
+// One workgroup (four waves) per sequence. The sequence's logical blocks are
+// cut into 64-block windows; wave w takes windows w, w+4, w+8, ... two at a
+// time, so each lane has two block-table entries, two expected tags and two
+// tag gathers in flight (coalesced table reads, a gather of the current
+// tags). A wave stops at its first window holding a failing block; the
+// lowest failing index inside a window is a ballot + find-first-set, and the
+// workgroup takes the minimum over its waves, so the verdict is
+// deterministic.
+#include <climits>
+
 #include "pda_internal.h"
 
 namespace pda {
@@ -28,37 +34,50 @@ constexpr int kThreads = 256;
 __global__ __launch_bounds__(kThreads) void validate_kernel(
     const uint32_t* __restrict__ page_tags, int P, const int32_t* __restrict__ block_table,
     const uint32_t* __restrict__ expected, int max_blocks, const int32_t* __restrict__ lens,
-    int B, int S, int32_t* __restrict__ verdict) {
-  const int s = (int)((blockIdx.x * (unsigned)kThreads + threadIdx.x) >> 6);
+    int S, int32_t* __restrict__ verdict) {
+  __shared__ int best[kThreads / 64];
+  const int s = blockIdx.x;
   const int lane = threadIdx.x & 63;
-  if (s >= B) return;
+  const int wave = threadIdx.x >> 6;
   const int64_t len = lens[s];
   if (len < 0 || len > (int64_t)max_blocks * S) {
-    if (lane == 0) verdict[s] = -1;
+    if (threadIdx.x == 0) verdict[s] = -1;
     return;
   }
   const int n = (int)((len + S - 1) / S);
   const int32_t* bt = block_table + (int64_t)s * max_blocks;
   const uint32_t* ex = expected + (int64_t)s * max_blocks;
-  int32_t result = 0;
-  for (int j0 = 0; j0 < n; j0 += 64) {
-    const int j = j0 + lane;
-    bool bad = false;
-    if (j < n) {
-      const int32_t p = bt[j];
-      const uint32_t want = ex[j];
-      if (p < 0 || p >= P)
-        bad = true;
-      else
-        bad = page_tags[p] != want;
+  constexpr int kStride = kThreads;           // blocks between a wave's windows
+  int first = INT_MAX;
+  for (int w0 = wave * 64; w0 < n; w0 += 2 * kStride) {
+    const int j0 = w0 + lane, j1 = w0 + kStride + lane;
+    int32_t p0 = 0, p1 = 0;
+    uint32_t e0 = 0, e1 = 0;
+    if (j0 < n) { p0 = bt[j0]; e0 = ex[j0]; }
+    if (j1 < n) { p1 = bt[j1]; e1 = ex[j1]; }
+    const bool r0 = j0 < n && (p0 < 0 || p0 >= P);
+    const bool r1 = j1 < n && (p1 < 0 || p1 >= P);
+    uint32_t t0 = e0, t1 = e1;
+    if (j0 < n && !r0) t0 = page_tags[p0];
+    if (j1 < n && !r1) t1 = page_tags[p1];
+    const uint64_t m0 = __ballot(r0 || t0 != e0);
+    const uint64_t m1 = __ballot(r1 || t1 != e1);
+    if (m0 != 0) {
+      first = w0 + __builtin_ctzll(m0);
+      break;
     }
-    const uint64_t mask = __ballot(bad);
-    if (mask != 0) {
-      result = j0 + __builtin_ctzll(mask) + 1;
+    if (m1 != 0) {
+      first = w0 + kStride + __builtin_ctzll(m1);
       break;
     }
   }
-  if (lane == 0) verdict[s] = result;
+  if (lane == 0) best[wave] = first;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int v = best[0];
+    for (int w = 1; w < kThreads / 64; ++w) v = min(v, best[w]);
+    verdict[s] = v == INT_MAX ? 0 : v + 1;
+  }
 }
 
 }  // namespace
@@ -76,10 +95,8 @@ extern "C" int validate_page_tags(const uint32_t* page_tags, int32_t num_pages,
   if (num_seqs == 0) return PDA_OK;
   if (!page_tags || !block_table || !expected_tags || !seq_lens || !verdict)
     return PDA_ERR_INVALID_ARG;
-  const int waves_per_block = kThreads / 64;
-  const int blocks = (num_seqs + waves_per_block - 1) / waves_per_block;
-  hipLaunchKernelGGL(validate_kernel, dim3(blocks), dim3(kThreads), 0, as_stream(stream),
+  hipLaunchKernelGGL(validate_kernel, dim3(num_seqs), dim3(kThreads), 0, as_stream(stream),
                      page_tags, num_pages, block_table, expected_tags, max_blocks_per_seq,
-                     seq_lens, num_seqs, page_size, verdict);
+                     seq_lens, page_size, verdict);
   return launch_status();
 }

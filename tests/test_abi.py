@@ -1,0 +1,116 @@
+"""The C ABI without a GPU: libpda.so loads, exports every function that
+include/pda.h declares, and rejects bad arguments with the documented status
+codes before anything is enqueued (no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pda.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([A-Za-z_]\w*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+@pytest.fixture(scope="module")
+def pda():
+    import decode_attention_fp8_write_amd as m
+    m.load()
+    return m
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert names == sorted(["kv_write_fp8", "kv_write_bf16", "validate_page_tags",
+                            "paged_decode_attn_workspace_bytes", "paged_decode_attn",
+                            "pda_status_string"])
+
+
+def test_library_exports_every_declared_symbol(pda):
+    lib = pda.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libpda.so does not export {name}"
+    assert set(pda.EXPORTS) == set(declared_functions())
+
+
+def test_status_strings(pda):
+    assert pda.status_string(pda.PDA_OK) == "ok"
+    assert pda.status_string(pda.PDA_ERR_INVALID_ARG) == "invalid argument"
+    assert pda.status_string(pda.PDA_ERR_UNSUPPORTED) == "unsupported shape or dtype"
+    assert pda.status_string(pda.PDA_ERR_LAUNCH) == "kernel launch failed"
+    assert pda.status_string(pda.PDA_ERR_WORKSPACE) == "workspace too small"
+    assert pda.status_string(99) == "unknown status"
+
+
+def _shape(pda, **kw):
+    base = dict(num_seqs=64, num_q_heads=64, num_kv_heads=8, head_dim_qk=128, head_dim_v=128,
+                page_size=16, num_pages=32768, max_blocks_per_seq=512,
+                kv_dtype=pda.KV_FP8_E4M3, scale_mode=pda.SCALE_PER_HEAD, split_tokens=512,
+                sm_scale=0.08838834764831845)
+    base.update(kw)
+    return pda.make_shape(**base)
+
+
+def test_workspace_sizes(pda):
+    # 64 seqs x 16 chunks of 512 x 8 kv heads, each 8 rows x (128 + 2) fp32,
+    # after a 256-byte-aligned header of (64 + 65) ints
+    sh = _shape(pda)
+    assert pda.paged_decode_attn_workspace_bytes(sh, 8192) == 768 + 64 * 16 * 8 * 8 * 130 * 4
+    # invalid shapes give 0
+    for bad in (dict(num_q_heads=60), dict(num_kv_heads=0), dict(page_size=0),
+                dict(split_tokens=100), dict(kv_dtype=7), dict(sm_scale=float("nan"))):
+        assert pda.paged_decode_attn_workspace_bytes(_shape(pda, **bad), 8192) == 0, bad
+    assert pda.paged_decode_attn_workspace_bytes(sh, -1) == 0
+    # latent path: one partial of 128 x (512 + 4) fp32 per (workgroup + sequence)
+    lat = _shape(pda, num_q_heads=128, num_kv_heads=1, head_dim_qk=576, head_dim_v=512,
+                 page_size=64, kv_dtype=pda.KV_FP8_E4M3, scale_mode=pda.SCALE_PER_TOKEN,
+                 v_in_k=True, split_tokens=0, sm_scale=1.0 / 24)
+    n = pda.paged_decode_attn_workspace_bytes(lat, 32768)
+    slot = 128 * 516 * 4
+    assert n > 0 and (n - 768) % slot == 0 and (n - 768) // slot > 64
+
+
+def test_argument_checks_return_before_launch(pda):
+    lib = pda.load()
+    null = None
+    sh = _shape(pda)
+    # null device pointers
+    st = lib.paged_decode_attn(ctypes.byref(sh), null, null, null, null, null, null, null, 8192,
+                               null, null, 0, null, null)
+    assert st == pda.PDA_ERR_INVALID_ARG
+    # unsupported head dim on an otherwise valid shape
+    sh2 = _shape(pda, head_dim_qk=96, head_dim_v=96)
+    fake = ctypes.c_void_p(256)
+    st = lib.paged_decode_attn(ctypes.byref(sh2), fake, fake, fake, fake, fake, fake, fake, 8192,
+                               null, fake, 1 << 20, fake, null)
+    assert st == pda.PDA_ERR_UNSUPPORTED
+    # workspace too small
+    st = lib.paged_decode_attn(ctypes.byref(sh), fake, fake, fake, fake, fake, fake, fake, 8192,
+                               null, fake, 16, fake, null)
+    assert st == pda.PDA_ERR_WORKSPACE
+    # kv_write: bad scale mode, per-token on a non-latent cache, bad sizes
+    st = lib.kv_write_fp8(fake, fake, fake, 4, 8, 128, 128, 16, 64, 7, fake, fake, null, fake,
+                          fake, null)
+    assert st == pda.PDA_ERR_INVALID_ARG
+    st = lib.kv_write_fp8(fake, fake, fake, 4, 8, 128, 128, 16, 64, pda.SCALE_PER_TOKEN, null,
+                          null, fake, fake, fake, null)
+    assert st == pda.PDA_ERR_UNSUPPORTED
+    st = lib.kv_write_bf16(fake, fake, fake, -1, 8, 128, 128, 16, 64, fake, fake, null)
+    assert st == pda.PDA_ERR_INVALID_ARG
+    st = lib.kv_write_bf16(fake, fake, fake, 4, 8, 100, 128, 16, 64, fake, fake, null)
+    assert st == pda.PDA_ERR_UNSUPPORTED
+    # zero tokens / zero sequences are valid no-ops
+    assert lib.kv_write_bf16(fake, fake, fake, 0, 8, 128, 128, 16, 64, fake, fake, null) == 0
+    assert lib.validate_page_tags(null, 64, null, null, 16, null, 0, 16, null, null) == 0
+    # validate: non-positive sizes, null pointers
+    assert lib.validate_page_tags(fake, 0, fake, fake, 16, fake, 4, 16, fake, null) == \
+        pda.PDA_ERR_INVALID_ARG
+    assert lib.validate_page_tags(null, 64, fake, fake, 16, fake, 4, 16, fake, null) == \
+        pda.PDA_ERR_INVALID_ARG
