@@ -376,23 +376,45 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
   }
   bool bad = false;
 
-  // Physical pages of the block starting at b0 (wave-uniform). Pages past the
-  // end of the chunk are replaced by the chunk's first page, a page of this
-  // sequence; their tokens are masked out below. A page id outside [0, P) is
-  // never dereferenced: it marks the item bad.
+  // Physical pages of the block starting at b0 (wave-uniform), in two steps:
+  // raw_pages issues the block-table loads (one scalar load of the NP
+  // consecutive entries when the whole block lies inside the chunk) a block
+  // ahead of their use; fix_pages checks them when the block comes up. Pages
+  // past the end of the chunk are replaced by the chunk's first page, a page
+  // of this sequence; their tokens are masked out below. A page id outside
+  // [0, P) is never dereferenced: it marks the item bad.
   int fb = btrow[tok0 / S];
   if (fb < 0 || fb >= a.P) {
     bad = true;
     fb = 0;
   }
-  auto pages_of = [&](int b0, Pages& pg) {
+  auto raw_pages = [&](int b0, Pages& r) {
+    r.p0 = r.p1 = r.p2 = r.p3 = fb;
+    if (b0 + 64 <= tok1) {
+      if constexpr (NP == 4) {
+        typedef int32_t i32x4 __attribute__((ext_vector_type(4), aligned(4)));
+        const i32x4 v = *(const __attribute__((address_space(4))) i32x4*)(btrow + b0 / S);
+        r.p0 = v.x; r.p1 = v.y; r.p2 = v.z; r.p3 = v.w;
+      } else if constexpr (NP == 2) {
+        typedef int32_t i32x2 __attribute__((ext_vector_type(2), aligned(4)));
+        const i32x2 v = *(const __attribute__((address_space(4))) i32x2*)(btrow + b0 / S);
+        r.p0 = v.x; r.p1 = v.y;
+      } else {
+        r.p0 = btrow[b0 / S];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < NP; ++k)
+        if (b0 + k * S < tok1) r.set(k, btrow[(b0 + k * S) / S]);
+    }
+  };
+  auto fix_pages = [&](int b0, const Pages& r, Pages& pg) {
     pg.p1 = pg.p2 = pg.p3 = fb;
 #pragma unroll
     for (int k = 0; k < NP; ++k) {
-      const int t = b0 + k * S;
       int p = fb;
-      if (t < tok1) {
-        p = btrow[t / S];
+      if (b0 + k * S < tok1) {
+        p = r.get(k);
         if (p < 0 || p >= a.P) {
           bad = true;
           p = fb;
@@ -405,9 +427,11 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
   // FP8 keys go through the wave's LDS buffer; BF16 keys through registers
   uint4 kk[FP8 ? 1 : I::KQ];
   W vv[32];
-  Pages pg;
+  Pages pg, raw;
   int b0 = tok0;
-  pages_of(b0, pg);
+  raw_pages(b0, raw);
+  fix_pages(b0, raw, pg);
+  if (b0 + 64 < tok1) raw_pages(b0 + 64, raw);
   if constexpr (FP8)
     dma_k<S>(a, g, pg, kw);
   else
@@ -419,7 +443,10 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
     const bool has_next = bn < tok1;
     const bool tail = b0 + 64 > tok1;
     Pages npg = pg;
-    if (has_next) pages_of(bn, npg);
+    if (has_next) {
+      fix_pages(bn, raw, npg);
+      if (bn + 64 < tok1) raw_pages(bn + 64, raw);
+    }
 
     // ---- QK: lane = token b0 + lane ------------------------------------
     float z[G];
@@ -434,32 +461,52 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
       // flight; the 32 V loads of this block came before it and the next
       // block's V loads are not issued yet) must have landed.
       __builtin_amdgcn_s_waitcnt(0x8F70);   // vmcnt(32): all but the 32 V loads
-      uint32_t qb[3][8];
+      // q in batches of QB steps, double-buffered: batch j+1 is issued right
+      // after the first dot products of batch j (which waited for batch j),
+      // so each wait is for loads issued QB-1 steps earlier. Scalar loads
+      // complete out of order, so any wait is for all of them.
+      constexpr int QB = (8 * G) % 4 == 0 ? 4 : 1;
+      uint32_t qa[QB][8], qc[QB][8];
       auto loadq = [&](int k, uint32_t(&dst)[8]) {
         cu32_t* qp = fence_ptr_after<G>(qbase, z);
         const int c16 = k / G, r = k % G;
 #pragma unroll
         for (int j = 0; j < 8; ++j) dst[j] = qp[r * 64 + c16 * 8 + j];
       };
-      loadq(0, qb[0]);
-      if constexpr (8 * G > 1) loadq(1, qb[1]);
+#pragma unroll
+      for (int i = 0; i < QB; ++i) loadq(i, qa[i]);
+      // keys of column group c16 (16 codes of the lane's token), read from
+      // LDS one group ahead of their conversion
+      auto readk = [&](int c16) -> uint4 {
+        return *reinterpret_cast<const uint4*>(kw + c16 * 1024 + lane * 16);
+      };
+      uint4 kcur = readk(0), knext = kcur;
       bf16x2_t kp[8];
       static_for<0, 8 * G>::run([&](auto K) {
         constexpr int k = decltype(K)::value;
         constexpr int c16 = k / G, r = k % G;
+        constexpr int jb = k / QB, ib = k % QB;
         if constexpr (r == 0) {
-          const uint4 w = *reinterpret_cast<const uint4*>(kw + c16 * 1024 + lane * 16);
+          const uint4 w = (c16 % 2 == 0) ? kcur : knext;
+          if constexpr (c16 + 1 < 8) {
+            if constexpr (c16 % 2 == 0) knext = readk(c16 + 1); else kcur = readk(c16 + 1);
+          }
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             kp[2 * j] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u4_get(w, j), 1.0f, false);
             kp[2 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u4_get(w, j), 1.0f, true);
           }
         }
-        if constexpr (k + 2 < 8 * G) loadq(k + 2, qb[(k + 2) % 3]);
+        uint32_t(&cur)[QB][8] = (jb % 2 == 0) ? qa : qc;
+        uint32_t(&nxt)[QB][8] = (jb % 2 == 0) ? qc : qa;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          z[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qb[k % 3][j]),
+          z[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, cur[ib][j]),
                                                  kp[j], z[r], false);
+        if constexpr (ib == 0 && (jb + 1) * QB < 8 * G) {
+#pragma unroll
+          for (int i = 0; i < QB; ++i) loadq((jb + 1) * QB + i, nxt[i]);
+        }
         if constexpr (r == G - 1) __builtin_amdgcn_sched_barrier(0);
       });
       // every key read of this block has been consumed: the buffer is free
@@ -620,18 +667,24 @@ void attn_partial_kernel(AttnArgs a) {
   const int total_sc = build_plan(a, S, pref, tmp, chunk);
   const long long total_items = (long long)total_sc * a.Hkv;
   const long long nw = (long long)gridDim.x * kWaves;
-  for (long long item = (long long)blockIdx.x * kWaves + wave; item < total_items; item += nw) {
-    const int sc = (int)(item / a.Hkv);
-    const int g = (int)(item % a.Hkv);
-    // sequence owning seq-chunk sc: last s with pref[s] <= sc
-    int lo = 0, hi = a.B;  // invariant pref[lo] <= sc < pref[hi]
+  // Work index w runs over (sequence, kv head, chunk) with the chunk fastest,
+  // so the waves of a workgroup usually share one (sequence, kv head) and its
+  // query rows stay in the scalar cache. The partial of (s, c, g) is stored
+  // at item (pref[s] + c) * Hkv + g.
+  for (long long w = (long long)blockIdx.x * kWaves + wave; w < total_items; w += nw) {
+    // sequence owning w: last s with pref[s] * Hkv <= w
+    int lo = 0, hi = a.B;  // invariant pref[lo] * Hkv <= w < pref[hi] * Hkv
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (pref[mid] <= sc) lo = mid; else hi = mid;
+      if ((long long)pref[mid] * a.Hkv <= w) lo = mid; else hi = mid;
     }
     const int s = __builtin_amdgcn_readfirstlane(lo);
-    const int c = __builtin_amdgcn_readfirstlane(sc - pref[lo]);
-    process_item<G, FP8, S>(a, s, c, __builtin_amdgcn_readfirstlane(g), chunk, item, pw, kw);
+    const int nc = pref[s + 1] - pref[s];
+    const int local = (int)(w - (long long)pref[s] * a.Hkv);
+    const int g = __builtin_amdgcn_readfirstlane(local / nc);
+    const int c = __builtin_amdgcn_readfirstlane(local % nc);
+    const long long item = (long long)(pref[s] + c) * a.Hkv + g;
+    process_item<G, FP8, S>(a, s, c, g, chunk, item, pw, kw);
   }
 }
 
