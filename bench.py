@@ -84,6 +84,8 @@ def time_steps(db, steps, warmup, torch):
     att = [e[2].elapsed_time(e[3]) for e in ev]
     step = [e[0].elapsed_time(e[3]) for e in ev]
     mean = lambda xs: sum(xs) / len(xs)
+    q = sorted(att)
+    log(f"attention call ms: min {q[0]:.4f} median {q[len(q) // 2]:.4f} max {q[-1]:.4f}")
     return dict(wall_ms_per_step=wall * 1e3 / steps, step_ms=mean(step), kv_write_ms=mean(kvw),
                 validate_ms=mean(val), attn_ms=mean(att),
                 attn_ms_min=min(att), attn_ms_max=max(att))
@@ -182,8 +184,8 @@ def other_workload(args, torch, np, synth, pda, workload):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--workload", type=int, default=WORKLOAD_ID, choices=(2, 3, 4, 5),
