@@ -246,12 +246,19 @@ void latent_partial_kernel(LatArgs a) {
         page = 0;
       }
       const uint8_t* src = a.kc + (int64_t)page * kPageBytes;
+      // Issued as inline asm: the compiler would make the first LDS read
+      // after a copy it can see wait for all of it, which serialises the
+      // copy of page j+1 with the arithmetic of page j. The wait at the top
+      // of the page loop (all vector memory, then a barrier) covers it.
+      const uint32_t l0 = __builtin_amdgcn_readfirstlane(
+          (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)pb.codes));
 #pragma unroll
       for (int ii = 0; ii < kWaveChunks / NW; ++ii) {
         const int i = ii * NW + wave;
-        __builtin_amdgcn_global_load_lds(
-            (const void __attribute__((address_space(1)))*)(src + (i * 64 + lane) * 16),
-            (void __attribute__((address_space(3)))*)(pb.codes + i * 1024), 16, 0, 0);
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :: "s"(__builtin_amdgcn_readfirstlane(l0 + i * 1024)),
+                        "v"(src + (i * 64 + lane) * 16)
+                     : "memory");
       }
       if (tid < kS) sc_next = a.tscale[(int64_t)page * kS + tid];
     };
