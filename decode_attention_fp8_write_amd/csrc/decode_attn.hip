@@ -88,8 +88,15 @@ __device__ __forceinline__ int n_chunks_of(const AttnArgs& a, int s, int S, int 
   return (len + chunk - 1) / chunk;
 }
 
+// Chunk slots of a sequence: its chunk count rounded up to a multiple of the
+// waves of a workgroup (one work unit = kWaves consecutive chunks of one
+// (sequence, kv head), one per wave).
+__device__ __forceinline__ int n_slots_of(const AttnArgs& a, int s, int S, int chunk) {
+  return (n_chunks_of(a, s, S, chunk) + kWaves - 1) / kWaves * kWaves;
+}
+
 // Every workgroup derives the same plan: chunk size (doubled until the
-// partials fit the workspace) and the exclusive prefix of chunks per
+// partials fit the workspace) and the exclusive prefix of chunk slots per
 // sequence, kept in LDS (pref[0..B]). Workgroup 0 also publishes it.
 __device__ int build_plan(const AttnArgs& a, int S, int* pref, int* tmp, int& chunk_out) {
   const int tid = threadIdx.x;
@@ -100,7 +107,7 @@ __device__ int build_plan(const AttnArgs& a, int S, int* pref, int* tmp, int& ch
   int total = 0;
   for (;;) {
     int local = 0;
-    for (int s = beg; s < end; ++s) local += n_chunks_of(a, s, S, chunk);
+    for (int s = beg; s < end; ++s) local += n_slots_of(a, s, S, chunk);
     tmp[tid] = local;
     __syncthreads();
     if (tid == 0) {
@@ -116,7 +123,7 @@ __device__ int build_plan(const AttnArgs& a, int S, int* pref, int* tmp, int& ch
     int run = tmp[tid];
     for (int s = beg; s < end; ++s) {
       pref[s] = run;
-      run += n_chunks_of(a, s, S, chunk);
+      run += n_slots_of(a, s, S, chunk);
     }
     total = tmp[kThreads];
     __syncthreads();
@@ -164,6 +171,19 @@ __device__ __forceinline__ cu32_t* fence_ptr_after(cu32_t* p, float (&z)[R]) {
 
 __device__ __forceinline__ uint32_t u4_get(const uint4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
+// acc + dot(q, k) over one bf16 pair, where q is taken from lane L of the
+// lane's 16-lane row (DPP row_newbcast). Written as inline asm because the
+// compiler does not fold the broadcast into v_dot2c. The q register is only
+// ever written by an LDS read (never by a VALU instruction just before a
+// DPP read of it), so no wait states are needed.
+template <int L>
+__device__ __forceinline__ float dot2_bcast(float acc, uint32_t q, bf16x2_t k) {
+  asm("v_dot2c_f32_bf16_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+      : "+v"(acc)
+      : "v"(q), "v"(k), "n"(L));
+  return acc;
 }
 
 // Bytes of the per-wave p buffer in LDS: G rows x 64 tokens of f16 (FP8
@@ -355,7 +375,7 @@ __device__ __forceinline__ void pv_block(
 
 template <int G, bool FP8, int S>
 __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, long long item,
-                             uint16_t* pw, uint8_t* kw) {
+                             uint16_t* pw, uint8_t* kw, const uint32_t* qs) {
   using I = Item<G, FP8, S>;
   using W = typename I::vword_t;
   constexpr int NP = I::NP;
@@ -454,60 +474,48 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
     for (int r = 0; r < G; ++r) z[r] = 0.0f;
     if constexpr (FP8) {
       // Keys from the wave's LDS buffer, 16 dims (one 16-byte read) at a
-      // time; q from SGPRs, one 8-dword scalar load per (16 dims, row),
-      // issued two steps ahead (a ring of three). The fence ties each load
-      // to the scores computed so far, so loads cannot be hoisted early.
-      // The key copy of this block (the oldest vector-memory operations in
-      // flight; the 32 V loads of this block came before it and the next
-      // block's V loads are not issued yet) must have landed.
+      // time, read one column group ahead. The key copy of this block (the
+      // oldest vector-memory operations in flight; the 32 V loads of this
+      // block came before it and the next block's V loads are not issued
+      // yet) must have landed.
       __builtin_amdgcn_s_waitcnt(0x8F70);   // vmcnt(32): all but the 32 V loads
-      // q in batches of QB steps, double-buffered: batch j+1 is issued right
-      // after the first dot products of batch j (which waited for batch j),
-      // so each wait is for loads issued QB-1 steps earlier. Scalar loads
-      // complete out of order, so any wait is for all of them.
-      constexpr int QB = (8 * G) % 4 == 0 ? 4 : 1;
-      uint32_t qa[QB][8], qc[QB][8];
-      auto loadq = [&](int k, uint32_t(&dst)[8]) {
-        cu32_t* qp = fence_ptr_after<G>(qbase, z);
-        const int c16 = k / G, r = k % G;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dst[j] = qp[r * 64 + c16 * 8 + j];
+      // q of one column group (G rows x 8 dwords) sits in the unit's LDS
+      // rows; lane l of every 16-lane row reads dwords 4(l % 2G) .. +3, so
+      // dword d of the group is register d % 4 of lane d / 4 in each row,
+      // and a DPP row broadcast hands it to all lanes as the dot operand.
+      constexpr int QL = 2 * G;   // lanes holding one column group's q
+      auto readq = [&](int c16) -> uint4 {
+        return *reinterpret_cast<const uint4*>(qs + c16 * (8 * G) + (lane % QL) * 4);
       };
-#pragma unroll
-      for (int i = 0; i < QB; ++i) loadq(i, qa[i]);
-      // keys of column group c16 (16 codes of the lane's token), read from
-      // LDS one group ahead of their conversion
       auto readk = [&](int c16) -> uint4 {
         return *reinterpret_cast<const uint4*>(kw + c16 * 1024 + lane * 16);
       };
       uint4 kcur = readk(0), knext = kcur;
+      uint4 qcur = readq(0), qnext = qcur;
       bf16x2_t kp[8];
-      static_for<0, 8 * G>::run([&](auto K) {
-        constexpr int k = decltype(K)::value;
-        constexpr int c16 = k / G, r = k % G;
-        constexpr int jb = k / QB, ib = k % QB;
-        if constexpr (r == 0) {
-          const uint4 w = (c16 % 2 == 0) ? kcur : knext;
-          if constexpr (c16 + 1 < 8) {
-            if constexpr (c16 % 2 == 0) knext = readk(c16 + 1); else kcur = readk(c16 + 1);
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            kp[2 * j] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u4_get(w, j), 1.0f, false);
-            kp[2 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u4_get(w, j), 1.0f, true);
+      static_for<0, 8>::run([&](auto C) {
+        constexpr int c16 = decltype(C)::value;
+        const uint4 w = (c16 % 2 == 0) ? kcur : knext;
+        const uint4 qv = (c16 % 2 == 0) ? qcur : qnext;
+        if constexpr (c16 + 1 < 8) {
+          if constexpr (c16 % 2 == 0) {
+            knext = readk(c16 + 1);
+            qnext = readq(c16 + 1);
+          } else {
+            kcur = readk(c16 + 1);
+            qcur = readq(c16 + 1);
           }
         }
-        uint32_t(&cur)[QB][8] = (jb % 2 == 0) ? qa : qc;
-        uint32_t(&nxt)[QB][8] = (jb % 2 == 0) ? qc : qa;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          z[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, cur[ib][j]),
-                                                 kp[j], z[r], false);
-        if constexpr (ib == 0 && (jb + 1) * QB < 8 * G) {
-#pragma unroll
-          for (int i = 0; i < QB; ++i) loadq((jb + 1) * QB + i, nxt[i]);
+        for (int j = 0; j < 4; ++j) {
+          kp[2 * j] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u4_get(w, j), 1.0f, false);
+          kp[2 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u4_get(w, j), 1.0f, true);
         }
-        if constexpr (r == G - 1) __builtin_amdgcn_sched_barrier(0);
+        static_for<0, 8 * G>::run([&](auto D) {
+          constexpr int d = decltype(D)::value;   // dword of the group: row d/8, dims pair d%8
+          z[d / 8] = dot2_bcast<d / 4>(z[d / 8], u4_get(qv, d % 4), kp[d % 8]);
+        });
+        __builtin_amdgcn_sched_barrier(0);
       });
       // every key read of this block has been consumed: the buffer is free
       if (has_next) dma_k<S>(a, g, npg, kw);
@@ -657,34 +665,49 @@ __attribute__((amdgpu_waves_per_eu(partial_waves<G, FP8>(), partial_waves<G, FP8
 void attn_partial_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) int lds[];
   constexpr int PB = pbuf_bytes<G, FP8>();
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr int KB = FP8 ? 8192 : 0;   // per-wave key buffer (FP8)
+  constexpr int QB = FP8 ? G * kD * 2 : 0;   // the unit's q rows (FP8)
   uint16_t* pw = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(lds) + wave * PB);
   uint8_t* kw = reinterpret_cast<uint8_t*>(lds) + kWaves * PB + wave * KB;
-  int* tmp = lds + kWaves * (PB + KB) / 4;   // kThreads + 1
+  uint32_t* qs = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(lds) + kWaves * (PB + KB));
+  int* tmp = lds + (kWaves * (PB + KB) + QB) / 4;   // kThreads + 1
   int* pref = tmp + kThreads + 1;     // B + 1
   int chunk;
-  const int total_sc = build_plan(a, S, pref, tmp, chunk);
-  const long long total_items = (long long)total_sc * a.Hkv;
-  const long long nw = (long long)gridDim.x * kWaves;
-  // Work index w runs over (sequence, kv head, chunk) with the chunk fastest,
-  // so the waves of a workgroup usually share one (sequence, kv head) and its
-  // query rows stay in the scalar cache. The partial of (s, c, g) is stored
-  // at item (pref[s] + c) * Hkv + g.
-  for (long long w = (long long)blockIdx.x * kWaves + wave; w < total_items; w += nw) {
-    // sequence owning w: last s with pref[s] * Hkv <= w
-    int lo = 0, hi = a.B;  // invariant pref[lo] * Hkv <= w < pref[hi] * Hkv
+  const int total_slots = build_plan(a, S, pref, tmp, chunk);
+  // A work unit is kWaves consecutive chunk slots of one (sequence, kv
+  // head): wave w takes chunk slot w, so the workgroup shares one group of
+  // query rows, staged in LDS once per unit. Units run with the chunk group
+  // fastest. The partial of (s, c, g) is stored at item (pref[s] + c) * Hkv + g.
+  const long long total_units = (long long)(total_slots / kWaves) * a.Hkv;
+  for (long long u = blockIdx.x; u < total_units; u += gridDim.x) {
+    // sequence owning unit u: last s with (pref[s] / kWaves) * Hkv <= u
+    int lo = 0, hi = a.B;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if ((long long)pref[mid] * a.Hkv <= w) lo = mid; else hi = mid;
+      if ((long long)(pref[mid] / kWaves) * a.Hkv <= u) lo = mid; else hi = mid;
     }
     const int s = __builtin_amdgcn_readfirstlane(lo);
-    const int nc = pref[s + 1] - pref[s];
-    const int local = (int)(w - (long long)pref[s] * a.Hkv);
-    const int g = __builtin_amdgcn_readfirstlane(local / nc);
-    const int c = __builtin_amdgcn_readfirstlane(local % nc);
-    const long long item = (long long)(pref[s] + c) * a.Hkv + g;
-    process_item<G, FP8, S>(a, s, c, g, chunk, item, pw, kw);
+    const int ncq = (pref[s + 1] - pref[s]) / kWaves;
+    const int local = (int)(u - (long long)(pref[s] / kWaves) * a.Hkv);
+    const int g = __builtin_amdgcn_readfirstlane(local / ncq);
+    const int c = __builtin_amdgcn_readfirstlane((local % ncq) * kWaves + wave);
+    if constexpr (FP8) {
+      // q rows of (s, g) into LDS as [column group c16][row r][8 dwords]:
+      // the 8G dwords one QK step of 16 dims needs are contiguous
+      __syncthreads();   // the previous unit's reads of qs are done
+      const uint32_t* qg =
+          reinterpret_cast<const uint32_t*>(a.q + ((int64_t)s * a.Hq + (int64_t)g * G) * kD);
+      for (int i = threadIdx.x; i < G * kD / 2; i += kThreads) {
+        const int r = i / (kD / 2), w = i % (kD / 2);   // row, dword of the row
+        qs[((w / 8) * G + r) * 8 + (w % 8)] = qg[i];
+      }
+      __syncthreads();
+    }
+    if (c < n_chunks_of(a, s, S, chunk)) {
+      const long long item = (long long)(pref[s] + c) * a.Hkv + g;
+      process_item<G, FP8, S>(a, s, c, g, chunk, item, pw, kw, qs);
+    }
   }
 }
 
@@ -710,7 +733,8 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a, int 
     return;
   }
   const int* pref = a.ws_hdr + kHdrInts;
-  const int c0 = pref[s], c1 = pref[s + 1];
+  const int chunk = a.ws_hdr[0];
+  const int c0 = pref[s], c1 = c0 + (len + chunk - 1) / chunk;
   const int64_t stride = G * (kD + 2);
   // chunks are read eight at a time so that eight loads are in flight; the
   // merge order is the chunk order, so the result is deterministic
@@ -910,7 +934,8 @@ extern "C" size_t paged_decode_attn_workspace_bytes(const pda_attn_shape* shape,
   if (latent_supported(sh)) return latent_workspace_bytes(sh, max_seq_len);
   const int chunk = resolve_chunk(sh, max_seq_len);
   const long long ml = max_seq_len > 0 ? max_seq_len : 1;
-  const long long per_seq = (ml + chunk - 1) / chunk;
+  // chunk slots per sequence: chunks rounded up to a multiple of kWaves
+  const long long per_seq = ((ml + chunk - 1) / chunk + kWaves - 1) / kWaves * kWaves;
   const long long items = (long long)sh.num_seqs * per_seq * sh.num_kv_heads;
   return header_bytes(sh.num_seqs) + (size_t)items * item_bytes(sh);
 }
@@ -940,7 +965,8 @@ extern "C" int paged_decode_attn(const pda_attn_shape* shape, const void* q, con
   if (!fp8 && (k_scale || v_scale)) return PDA_ERR_INVALID_ARG;
   const size_t hdr = header_bytes(sh.num_seqs);
   const size_t ib = item_bytes(sh);
-  if (workspace_bytes < hdr + (size_t)sh.num_seqs * sh.num_kv_heads * ib) return PDA_ERR_WORKSPACE;
+  if (workspace_bytes < hdr + (size_t)sh.num_seqs * sh.num_kv_heads * kWaves * ib)
+    return PDA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return PDA_ERR_INVALID_ARG;
   const int G = sh.num_q_heads / sh.num_kv_heads;
   const int chunk = resolve_chunk(sh, max_seq_len);
@@ -969,13 +995,14 @@ extern "C" int paged_decode_attn(const pda_attn_shape* shape, const void* q, con
   const kernel_t pk = fp8 ? pick_partial<true>(G, sh.page_size) : pick_partial<false>(G, sh.page_size);
   const combine_t ck = fp8 ? pick_combine<true>(G) : pick_combine<false>(G);
   const size_t pbuf = (size_t)kWaves * ((size_t)(fp8 ? 1 : 2) * (size_t)G * 64 * 2 +
-                                          (fp8 ? 8192 : 0));
+                                          (fp8 ? 8192 : 0)) +
+                      (fp8 ? (size_t)G * kD * 2 : 0);
   const size_t lds = pbuf + (size_t)(kThreads + 1 + sh.num_seqs + 1) * sizeof(int);
   const long long ml = max_seq_len > 0 ? max_seq_len : 1;
-  const long long items_bound = (long long)sh.num_seqs * sh.num_kv_heads * ((ml + chunk - 1) / chunk);
+  const long long units_bound =
+      (long long)sh.num_seqs * sh.num_kv_heads * (((ml + chunk - 1) / chunk + kWaves - 1) / kWaves);
   long long grid = (long long)device_cu_count() * blocks_per_cu(pk, lds);
-  const long long need = (items_bound + kWaves - 1) / kWaves;
-  if (grid > need) grid = need;
+  if (grid > units_bound) grid = units_bound;
   if (grid < 1) grid = 1;
   hipStream_t s = as_stream(stream);
   hipLaunchKernelGGL(pk, dim3((unsigned)grid), dim3(kThreads), lds, s, a);
