@@ -173,6 +173,61 @@ __device__ __forceinline__ uint32_t u4_get(const uint4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
 
+// Two wait states after the conversions of one step, tied to their results
+// so that the inline-asm dots that read them cannot be scheduled closer: a
+// scaled conversion's result is not forwarded to an immediately following
+// instruction, and the compiler only pads consumers it can see.
+template <typename T>
+__device__ __forceinline__ void settle8(T (&v)[8]) {
+  asm volatile("s_nop 1"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                 "+v"(v[6]), "+v"(v[7]));
+}
+template <typename T>
+__device__ __forceinline__ void settle44(T (&a)[4], T (&b)[4]) {
+  asm volatile("s_nop 1"
+               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]),
+                 "+v"(b[2]), "+v"(b[3]));
+}
+
+// Wait states around runs of the inline-asm DPP dots, tied to the values
+// they accumulate: a dot product's result reaches a different instruction
+// only three wait states later (a following dot of the same kind reading it
+// as its accumulator is forwarded), and a DPP instruction reads no VGPR a
+// VALU instruction wrote in the two wait states before. The compiler pads
+// neither around inline asm. N = s_nop operand (N + 1 wait states).
+template <int N, int R>
+__device__ __forceinline__ void settle_rows(float (&z)[R]) {
+  if constexpr (R == 1) {
+    asm volatile("s_nop %1" : "+v"(z[0]) : "n"(N));
+  } else if constexpr (R == 2) {
+    asm volatile("s_nop %2" : "+v"(z[0]), "+v"(z[1]) : "n"(N));
+  } else if constexpr (R == 4) {
+    asm volatile("s_nop %4" : "+v"(z[0]), "+v"(z[1]), "+v"(z[2]), "+v"(z[3]) : "n"(N));
+  } else {
+    asm volatile("s_nop %8"
+                 : "+v"(z[0]), "+v"(z[1]), "+v"(z[2]), "+v"(z[3]), "+v"(z[4]), "+v"(z[5]),
+                   "+v"(z[6]), "+v"(z[7])
+                 : "n"(N));
+  }
+}
+template <int N, int G>
+__device__ __forceinline__ void settle_acc(float (&acc)[G][2]) {
+  float a0[G], a1[G];
+#pragma unroll
+  for (int r = 0; r < G; ++r) {
+    a0[r] = acc[r][0];
+    a1[r] = acc[r][1];
+  }
+  settle_rows<N>(a0);
+  settle_rows<N>(a1);
+#pragma unroll
+  for (int r = 0; r < G; ++r) {
+    acc[r][0] = a0[r];
+    acc[r][1] = a1[r];
+  }
+}
+
 // acc + dot(q, k) over one bf16 pair, where q is taken from lane L of the
 // lane's 16-lane row (DPP row_newbcast). Written as inline asm because the
 // compiler does not fold the broadcast into v_dot2c. The q register is only
@@ -305,6 +360,61 @@ __device__ __forceinline__ uint32_t pair_mask(int i, int valid) {
 // dim 2l+1: tokens 2i, 2i+1).
 __device__ __forceinline__ uint32_t code_pair_mask(int i, int valid) {
   return (2 * i < valid ? 0x00FF00FFu : 0u) | (2 * i + 1 < valid ? 0xFF00FF00u : 0u);
+}
+
+// acc + dot(p, v) over one f16 pair, p taken from lane L of the lane's
+// 16-lane row (DPP row_newbcast); inline asm for the same reason as
+// dot2_bcast, and p registers likewise only come from LDS reads.
+template <int L>
+__device__ __forceinline__ float dot2_bcast_f16(float acc, uint32_t p, f16x2_t v) {
+  asm("v_dot2c_f32_f16_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+      : "+v"(acc)
+      : "v"(p), "v"(v), "n"(L));
+  return acc;
+}
+
+// FP8 PV of one 64-token block for the lane's two dims. The softmax left p
+// in the wave's LDS buffer as [8-token group ic][row r][8 tokens] (f16), so
+// group ic's 4G dwords are contiguous: lane l of every 16-lane row reads
+// dwords 2(l % 2G), +1 of the group (one 8-byte read per group, one group
+// ahead), and the p pair (row r, token pair jj) is register jj % 2 of lane
+// 2r + jj/2, handed to the dot by a DPP row broadcast.
+template <int G, bool TAIL>
+__device__ __forceinline__ void pv_block_fp8(const uint32_t (&vv)[32], const uint16_t* pw,
+                                             float (&acc)[G][2], int valid) {
+  const int lane = __lane_id();
+  auto rdp = [&](int ic) -> uint2 {
+    return *reinterpret_cast<const uint2*>(pw + ic * (8 * G) + (lane % (2 * G)) * 4);
+  };
+  uint2 pa = rdp(0), pb = pa;
+  settle_acc<1, G>(acc);
+  static_for<0, 8>::run([&](auto IC) {
+    constexpr int ic = decltype(IC)::value;
+    const uint2 pc = (ic % 2 == 0) ? pa : pb;
+    if constexpr (ic + 1 < 8) {
+      if constexpr (ic % 2 == 0) pb = rdp(ic + 1); else pa = rdp(ic + 1);
+    }
+    f16x2_t v0[4], v1[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t w = vv[4 * ic + j];
+      // bytes: (dim 2l, token 2i), (2l, 2i+1), (2l+1, 2i), (2l+1, 2i+1)
+      if constexpr (TAIL) w &= code_pair_mask(4 * ic + j, valid);
+      v0[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+      v1[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+    }
+    settle44(v0, v1);
+    static_for<0, 4 * G>::run([&](auto D) {
+      constexpr int d = decltype(D)::value;   // row d/4, token pair d%4 of the group
+      constexpr int r = d / 4, jj = d % 4;
+      const uint32_t pr = (jj % 2 == 0) ? pc.x : pc.y;
+      acc[r][0] = dot2_bcast_f16<2 * r + jj / 2>(acc[r][0], pr, v0[jj]);
+      acc[r][1] = dot2_bcast_f16<2 * r + jj / 2>(acc[r][1], pr, v1[jj]);
+    });
+    // keep the schedule in program order (see pv_block)
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  settle_acc<2, G>(acc);
 }
 
 template <int G, bool FP8, bool TAIL>
@@ -493,6 +603,7 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
       uint4 kcur = readk(0), knext = kcur;
       uint4 qcur = readq(0), qnext = qcur;
       bf16x2_t kp[8];
+      settle_rows<1>(z);
       static_for<0, 8>::run([&](auto C) {
         constexpr int c16 = decltype(C)::value;
         const uint4 w = (c16 % 2 == 0) ? kcur : knext;
@@ -511,12 +622,14 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
           kp[2 * j] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u4_get(w, j), 1.0f, false);
           kp[2 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u4_get(w, j), 1.0f, true);
         }
+        settle8(kp);
         static_for<0, 8 * G>::run([&](auto D) {
           constexpr int d = decltype(D)::value;   // dword of the group: row d/8, dims pair d%8
           z[d / 8] = dot2_bcast<d / 4>(z[d / 8], u4_get(qv, d % 4), kp[d % 8]);
         });
         __builtin_amdgcn_sched_barrier(0);
       });
+      settle_rows<2>(z);
       // every key read of this block has been consumed: the buffer is free
       if (has_next) dma_k<S>(a, g, npg, kw);
     } else {
@@ -594,14 +707,15 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
         }
       }
     }
-    // p of this lane's token for every row, to the wave's LDS buffer:
-    // pw[r*64 + t] (f16), or hi/lo bf16 parts at pw and pw + G*64.
+    // p of this lane's token for every row, to the wave's LDS buffer: FP8
+    // as [t/8][r][t%8] (f16, the order pv_block_fp8 reads), BF16 as
+    // pw[r*64 + t] with hi/lo bf16 parts at pw and pw + G*64.
 #pragma unroll
     for (int r = 0; r < G; ++r) {
       const float p = __builtin_amdgcn_exp2f(zl[r]);
       l[r] += p;
       if constexpr (FP8) {
-        pw[r * 64 + lane] = __builtin_bit_cast(uint16_t, (_Float16)p);
+        pw[(lane / 8) * (8 * G) + r * 8 + (lane % 8)] = __builtin_bit_cast(uint16_t, (_Float16)p);
       } else {
         const uint32_t pu = as_u32(p);
         const float rem = p - as_f32(pu & 0xFFFF0000u);
@@ -621,10 +735,16 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
     // (the empty asm keeps the two copies from being merged back into one)
     if (tail) {
       asm volatile("" ::: "memory");
-      pv_block<G, FP8, true>(vv, pw, acc, tok1 - b0);
+      if constexpr (FP8)
+        pv_block_fp8<G, true>(vv, pw, acc, tok1 - b0);
+      else
+        pv_block<G, FP8, true>(vv, pw, acc, tok1 - b0);
     } else {
       asm volatile("" ::: "memory");
-      pv_block<G, FP8, false>(vv, pw, acc, 64);
+      if constexpr (FP8)
+        pv_block_fp8<G, false>(vv, pw, acc, 64);
+      else
+        pv_block<G, FP8, false>(vv, pw, acc, 64);
     }
     if (!has_next) break;
     load_v<G, FP8, S>(a, g, npg, vv);
