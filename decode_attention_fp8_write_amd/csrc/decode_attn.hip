@@ -856,29 +856,13 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a, int 
   const int chunk = a.ws_hdr[0];
   const int c0 = pref[s], c1 = c0 + (len + chunk - 1) / chunk;
   const int64_t stride = G * (kD + 2);
-  // chunks are read eight at a time so that eight loads are in flight; the
-  // merge order is the chunk order, so the result is deterministic
-  constexpr int kB = 8;
-  float M = -INFINITY;
-  bool nan = false;
-  for (int c = c0; c < c1; c += kB) {
-    float mc[kB];
-#pragma unroll
-    for (int i = 0; i < kB; ++i)
-      mc[i] = (c + i < c1) ? a.ws_part[((int64_t)(c + i) * a.Hkv + g) * stride + G * kD + r]
-                           : -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kB; ++i) {
-      nan |= __builtin_isnan(mc[i]);
-      M = fmaxf(M, mc[i]);
-    }
-  }
-  if (nan) {
-    *reinterpret_cast<float4*>(o) = make_float4(qnan, qnan, qnan, qnan);
-    return;
-  }
-  float L = 0.0f;
+  // Chunks are read sixteen at a time, all of a batch's loads (max, sum,
+  // four dims) issued together; batches merge into the running result with
+  // the same log-sum-exp rule (one pass, chunk order, deterministic).
+  constexpr int kB = 16;
+  float M = -INFINITY, L = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  bool nan = false;
   for (int c = c0; c < c1; c += kB) {
     float mc[kB], lc[kB];
     float4 v[kB];
@@ -895,6 +879,21 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a, int 
         v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
+    float Mb = M;
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      nan |= __builtin_isnan(mc[i]);
+      Mb = fmaxf(Mb, mc[i]);
+    }
+    if (Mb > M) {   // every chunk holds a valid token, so Mb is finite here
+      const float alpha = __builtin_amdgcn_exp2f(M - Mb);   // 0 while M = -inf
+      L *= alpha;
+      acc.x *= alpha;
+      acc.y *= alpha;
+      acc.z *= alpha;
+      acc.w *= alpha;
+      M = Mb;
+    }
 #pragma unroll
     for (int i = 0; i < kB; ++i) {
       const float w = __builtin_amdgcn_exp2f(mc[i] - M);
@@ -904,6 +903,10 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a, int 
       acc.z += w * v[i].z;
       acc.w += w * v[i].w;
     }
+  }
+  if (nan) {
+    *reinterpret_cast<float4*>(o) = make_float4(qnan, qnan, qnan, qnan);
+    return;
   }
   const float f = (FP8 ? a.v_scale[g] : 1.0f) / L;
   *reinterpret_cast<float4*>(o) = make_float4(acc.x * f, acc.y * f, acc.z * f, acc.w * f);
