@@ -12,9 +12,12 @@
 //
 // Work decomposition. A sequence's context is cut into page-aligned chunks
 // (split-K). A work item is (sequence, chunk, kv head) and belongs to one
-// wavefront. Each workgroup first derives the item list from seq_lens and the
-// verdicts (aborted sequences get no items, so none of their pages is read),
-// then its waves take items round-robin. Partials (unnormalised output rows,
+// wavefront; a workgroup of four waves takes units of four consecutive chunk
+// slots of one (sequence, kv head), so the G query rows are staged in LDS once
+// per unit. Each workgroup first derives the slot list from seq_lens and the
+// verdicts (aborted sequences get no slots, so none of their pages is read;
+// a sequence's slot count is its chunk count rounded up to a multiple of
+// four, and a padding slot does nothing). Partials (unnormalised output rows,
 // running max, running sum) go to the workspace; the combine kernel merges
 // them with a log-sum-exp rule.
 //
@@ -22,8 +25,11 @@
 //  * QK: lane = token. FP8 keys reach the wave's own LDS buffer by direct
 //    global->LDS copies issued one block ahead (no registers hold them in
 //    flight); BF16 keys come through registers. Code pairs convert exactly to
-//    bf16 and v_dot2_f32_bf16 accumulates q.k for all G query rows, the q
-//    operand a wave-uniform SGPR pair fetched by scalar loads.
+//    bf16 and v_dot2_f32_bf16 accumulates q.k for all G query rows. For FP8
+//    the q pair is taken from another lane by a DPP row broadcast (lane
+//    2r + j of each row of 16 lanes holds dwords of row r, read from the
+//    unit's LDS copy of q); for BF16 it is a wave-uniform SGPR pair fetched
+//    by scalar loads.
 //  * softmax in log2 units with a lazy running max: it only moves when some
 //    score of the block exceeds it by more than kTau (a per-row ballot), so
 //    p <= 2^kTau and the wave-wide maximum is rarely needed.
@@ -32,11 +38,20 @@
 //  * PV: lane = two dims, all 64 tokens. The V format puts the two tokens of
 //    an even/odd slot pair next to each other, so one V word is (dim, 2
 //    tokens) x 2 dims; its codes convert exactly to two f16 pairs and
-//    v_dot2_f32_f16 takes the matching p pair, read from LDS as a broadcast
-//    (one 16-byte read gives a row's four p pairs).
+//    v_dot2_f32_f16 takes the matching p pair. For FP8 one 8-byte LDS read
+//    per lane brings the p of 8 tokens of one row, and a DPP row broadcast
+//    hands each pair to every lane; for BF16 p comes as a 16-byte broadcast
+//    read.
 //  * V of the next block is loaded into registers once PV is done.
 // Every dot product accumulates in fp32; q enters exactly (bf16), K and V
 // codes convert exactly, and p is rounded once.
+//
+// gfx950 wait states that the compiler does not insert around inline asm,
+// which the DPP dots are: a DPP operand must not have been written by a VALU
+// instruction in the two instructions before, and a dot result may be read by
+// a different instruction only three instructions later (a chain of the same
+// dot opcode through its accumulator is forwarded). The s_nop helpers below
+// pad exactly these places, and a test checks the emitted assembly.
 #include <mutex>
 #include <type_traits>
 
