@@ -17,9 +17,11 @@
 // per unit. Each workgroup first derives the slot list from seq_lens and the
 // verdicts (aborted sequences get no slots, so none of their pages is read;
 // a sequence's slot count is its chunk count rounded up to a multiple of
-// four, and a padding slot does nothing). Partials (unnormalised output rows,
-// running max, running sum) go to the workspace; the combine kernel merges
-// them with a log-sum-exp rule.
+// four, and a padding slot does nothing). Each wave leaves its partial
+// (unnormalised output rows, running max, running sum) in LDS; the workgroup
+// merges the unit's four with a log-sum-exp rule and writes one partial per
+// unit to the workspace, and the combine kernel merges a sequence's units
+// with the same rule.
 //
 // Inside an item a wave walks 64 tokens (a block) at a time:
 //  * QK: lane = token. FP8 keys reach the wave's own LDS buffer by direct
@@ -77,11 +79,11 @@ struct AttnArgs {
   const int32_t* __restrict__ lens;
   const int32_t* __restrict__ verdict;
   int32_t* ws_hdr;      // [0] chunk tokens, [1] seq-chunks, then prefix[B+1]
-  float* ws_part;       // items * G * (D + 2)
+  float* ws_part;       // partials (one per unit and kv head) * G * (D + 2)
   float* out;
   int B, Hq, Hkv, P, max_blocks;
   int chunk0;           // requested chunk (tokens), multiple of 64 and S
-  long long cap_items;  // partials that fit in the workspace
+  long long cap_items;  // unit partials that fit in the workspace
   float sm_scale;
 };
 
@@ -111,7 +113,7 @@ __device__ __forceinline__ int n_slots_of(const AttnArgs& a, int s, int S, int c
 }
 
 // Every workgroup derives the same plan: chunk size (doubled until the
-// partials fit the workspace) and the exclusive prefix of chunk slots per
+// unit partials fit the workspace) and the exclusive prefix of chunk slots per
 // sequence, kept in LDS (pref[0..B]). Workgroup 0 also publishes it.
 __device__ int build_plan(const AttnArgs& a, int S, int* pref, int* tmp, int& chunk_out) {
   const int tid = threadIdx.x;
@@ -142,7 +144,7 @@ __device__ int build_plan(const AttnArgs& a, int S, int* pref, int* tmp, int& ch
     }
     total = tmp[kThreads];
     __syncthreads();
-    if ((long long)total * a.Hkv <= a.cap_items) break;
+    if ((long long)(total / kWaves) * a.Hkv <= a.cap_items) break;
     chunk *= 2;
   }
   if (tid == 0) pref[a.B] = total;
@@ -499,8 +501,8 @@ __device__ __forceinline__ void pv_block(
 }
 
 template <int G, bool FP8, int S>
-__device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, long long item,
-                             uint16_t* pw, uint8_t* kw, const uint32_t* qs) {
+__device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, uint16_t* pw,
+                             uint8_t* kw, const uint32_t* qs, float* mg) {
   using I = Item<G, FP8, S>;
   using W = typename I::vword_t;
   constexpr int NP = I::NP;
@@ -771,20 +773,65 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  // ---- write the partial ------------------------------------------------
-  float* part = a.ws_part + item * (int64_t)(G * (kD + 2));
-  if (bad) {
-    if (lane < G) part[G * kD + lane] = __builtin_nanf("");
-    return;
-  }
+  // ---- the partial, to the wave's merge slot in LDS ----------------------
+  // [G rows x 128 dims][G maxima][G sums]; a bad item's maxima are NaN.
+  // (For FP8 the slot is the key buffer, whose last copy was waited for
+  // before the last QK.)
 #pragma unroll
   for (int r = 0; r < G; ++r) {
     const float lt = wave_sum(l[r]);
-    *reinterpret_cast<float2*>(part + r * kD + 2 * lane) = make_float2(acc[r][0], acc[r][1]);
+    *reinterpret_cast<float2*>(mg + r * kD + 2 * lane) = make_float2(acc[r][0], acc[r][1]);
     if (lane == r) {
-      part[G * kD + r] = m[r];
-      part[G * kD + G + r] = lt;
+      mg[G * kD + r] = bad ? __builtin_nanf("") : m[r];
+      mg[G * kD + G + r] = lt;
     }
+  }
+}
+
+// Bytes of one partial, G rows x (128 dims + max + sum) fp32, rounded up to
+// 16 so that every LDS merge slot is aligned for 16-byte reads.
+template <int G>
+constexpr int partial_bytes() {
+  return (G * (kD + 2) * 4 + 15) / 16 * 16;
+}
+
+// Merge the partials the waves of a unit left in their LDS slots (nv of
+// them, in chunk order) into one partial in the workspace: the log-sum-exp
+// rule, M = max m_w, L = sum 2^(m_w - M) l_w, acc = sum 2^(m_w - M) acc_w. A
+// NaN maximum (a bad item) makes the merged maximum NaN.
+template <int G>
+__device__ void merge_unit(const float* mg0, int slot_stride, int nv, float* part) {
+  const int r = threadIdx.x >> 5;
+  const int d4 = (threadIdx.x & 31) * 4;
+  if (r >= G) return;
+  float mw[kWaves];
+  float M = -INFINITY;
+  bool nan = false;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    mw[w] = w < nv ? mg0[w * slot_stride + G * kD + r] : -INFINITY;
+    nan |= __builtin_isnan(mw[w]);
+    M = fmaxf(M, mw[w]);
+  }
+  float L = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < nv) {
+      const float* pw = mg0 + w * slot_stride;
+      const float e = __builtin_amdgcn_exp2f(mw[w] - M);
+      const float4 v = *reinterpret_cast<const float4*>(pw + r * kD + d4);
+      L += e * pw[G * kD + G + r];
+      acc.x += e * v.x;
+      acc.y += e * v.y;
+      acc.z += e * v.z;
+      acc.w += e * v.w;
+    }
+  }
+  *reinterpret_cast<float4*>(part + r * kD + d4) = acc;
+  if (d4 == 0) {
+    part[G * kD + r] = nan ? __builtin_nanf("") : M;
+    part[G * kD + G + r] = L;
   }
 }
 
@@ -806,14 +853,21 @@ void attn_partial_kernel(AttnArgs a) {
   uint16_t* pw = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(lds) + wave * PB);
   uint8_t* kw = reinterpret_cast<uint8_t*>(lds) + kWaves * PB + wave * KB;
   uint32_t* qs = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(lds) + kWaves * (PB + KB));
-  int* tmp = lds + (kWaves * (PB + KB) + QB) / 4;   // kThreads + 1
+  // merge slots: the key buffers (FP8), else a region of their own
+  constexpr int MB = FP8 ? 0 : kWaves * partial_bytes<G>();
+  static_assert(!FP8 || partial_bytes<G>() <= KB, "a partial must fit a key buffer");
+  float* mg0 = reinterpret_cast<float*>(FP8 ? reinterpret_cast<char*>(lds) + kWaves * PB
+                                            : reinterpret_cast<char*>(lds) + kWaves * PB + QB);
+  constexpr int MS = (FP8 ? KB : partial_bytes<G>()) / 4;   // slot stride, floats
+  int* tmp = lds + (kWaves * (PB + KB) + QB + MB) / 4;   // kThreads + 1
   int* pref = tmp + kThreads + 1;     // B + 1
   int chunk;
   const int total_slots = build_plan(a, S, pref, tmp, chunk);
   // A work unit is kWaves consecutive chunk slots of one (sequence, kv
   // head): wave w takes chunk slot w, so the workgroup shares one group of
   // query rows, staged in LDS once per unit. Units run with the chunk group
-  // fastest. The partial of (s, c, g) is stored at item (pref[s] + c) * Hkv + g.
+  // fastest. The merged partial of unit j of (s, g) is stored at
+  // (pref[s] / kWaves + j) * Hkv + g.
   const long long total_units = (long long)(total_slots / kWaves) * a.Hkv;
   for (long long u = blockIdx.x; u < total_units; u += gridDim.x) {
     // sequence owning unit u: last s with (pref[s] / kWaves) * Hkv <= u
@@ -826,11 +880,12 @@ void attn_partial_kernel(AttnArgs a) {
     const int ncq = (pref[s + 1] - pref[s]) / kWaves;
     const int local = (int)(u - (long long)(pref[s] / kWaves) * a.Hkv);
     const int g = __builtin_amdgcn_readfirstlane(local / ncq);
-    const int c = __builtin_amdgcn_readfirstlane((local % ncq) * kWaves + wave);
+    const int j = local % ncq;   // unit of (s, g)
+    const int c = __builtin_amdgcn_readfirstlane(j * kWaves + wave);
+    __syncthreads();   // the previous unit's reads of qs and the merge slots are done
     if constexpr (FP8) {
       // q rows of (s, g) into LDS as [column group c16][row r][8 dwords]:
       // the 8G dwords one QK step of 16 dims needs are contiguous
-      __syncthreads();   // the previous unit's reads of qs are done
       const uint32_t* qg =
           reinterpret_cast<const uint32_t*>(a.q + ((int64_t)s * a.Hq + (int64_t)g * G) * kD);
       for (int i = threadIdx.x; i < G * kD / 2; i += kThreads) {
@@ -839,14 +894,15 @@ void attn_partial_kernel(AttnArgs a) {
       }
       __syncthreads();
     }
-    if (c < n_chunks_of(a, s, S, chunk)) {
-      const long long item = (long long)(pref[s] + c) * a.Hkv + g;
-      process_item<G, FP8, S>(a, s, c, g, chunk, item, pw, kw, qs);
-    }
+    const int nch = n_chunks_of(a, s, S, chunk);
+    if (c < nch) process_item<G, FP8, S>(a, s, c, g, chunk, pw, kw, qs, mg0 + wave * MS);
+    __syncthreads();
+    float* part = a.ws_part + ((int64_t)(pref[s] / kWaves + j) * a.Hkv + g) * (G * (kD + 2));
+    merge_unit<G>(mg0, MS, min(kWaves, nch - j * kWaves), part);
   }
 }
 
-// Merge the chunk partials of one (sequence, kv head): G rows x 128 dims,
+// Merge the unit partials of one (sequence, kv head): G rows x 128 dims,
 // four dims per thread.
 template <int G, bool FP8>
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a, int S) {
@@ -868,12 +924,11 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a, int 
     return;
   }
   const int* pref = a.ws_hdr + kHdrInts;
-  const int chunk = a.ws_hdr[0];
-  const int c0 = pref[s], c1 = c0 + (len + chunk - 1) / chunk;
+  const int c0 = pref[s] / kWaves, c1 = pref[s + 1] / kWaves;
   const int64_t stride = G * (kD + 2);
-  // Chunks are read sixteen at a time, all of a batch's loads (max, sum,
-  // four dims) issued together; batches merge into the running result with
-  // the same log-sum-exp rule (one pass, chunk order, deterministic).
+  // Unit partials are read sixteen at a time, all of a batch's loads (max,
+  // sum, four dims) issued together; batches merge into the running result
+  // with the same log-sum-exp rule (one pass, chunk order, deterministic).
   constexpr int kB = 16;
   float M = -INFINITY, L = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -900,7 +955,7 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a, int 
       nan |= __builtin_isnan(mc[i]);
       Mb = fmaxf(Mb, mc[i]);
     }
-    if (Mb > M) {   // every chunk holds a valid token, so Mb is finite here
+    if (Mb > M) {   // every unit holds a valid token, so Mb is finite here
       const float alpha = __builtin_amdgcn_exp2f(M - Mb);   // 0 while M = -inf
       L *= alpha;
       acc.x *= alpha;
@@ -1072,8 +1127,8 @@ extern "C" size_t paged_decode_attn_workspace_bytes(const pda_attn_shape* shape,
   if (latent_supported(sh)) return latent_workspace_bytes(sh, max_seq_len);
   const int chunk = resolve_chunk(sh, max_seq_len);
   const long long ml = max_seq_len > 0 ? max_seq_len : 1;
-  // chunk slots per sequence: chunks rounded up to a multiple of kWaves
-  const long long per_seq = ((ml + chunk - 1) / chunk + kWaves - 1) / kWaves * kWaves;
+  // units per sequence: chunks in groups of kWaves (one merged partial each)
+  const long long per_seq = ((ml + chunk - 1) / chunk + kWaves - 1) / kWaves;
   const long long items = (long long)sh.num_seqs * per_seq * sh.num_kv_heads;
   return header_bytes(sh.num_seqs) + (size_t)items * item_bytes(sh);
 }
@@ -1103,7 +1158,9 @@ extern "C" int paged_decode_attn(const pda_attn_shape* shape, const void* q, con
   if (!fp8 && (k_scale || v_scale)) return PDA_ERR_INVALID_ARG;
   const size_t hdr = header_bytes(sh.num_seqs);
   const size_t ib = item_bytes(sh);
-  if (workspace_bytes < hdr + (size_t)sh.num_seqs * sh.num_kv_heads * kWaves * ib)
+  // the plan doubles the chunk until the partials fit; it cannot go below one
+  // unit per (sequence, kv head)
+  if (workspace_bytes < hdr + (size_t)sh.num_seqs * sh.num_kv_heads * ib)
     return PDA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return PDA_ERR_INVALID_ARG;
   const int G = sh.num_q_heads / sh.num_kv_heads;
@@ -1134,7 +1191,7 @@ extern "C" int paged_decode_attn(const pda_attn_shape* shape, const void* q, con
   const combine_t ck = fp8 ? pick_combine<true>(G) : pick_combine<false>(G);
   const size_t pbuf = (size_t)kWaves * ((size_t)(fp8 ? 1 : 2) * (size_t)G * 64 * 2 +
                                           (fp8 ? 8192 : 0)) +
-                      (fp8 ? (size_t)G * kD * 2 : 0);
+                      (fp8 ? (size_t)G * kD * 2 : (size_t)kWaves * ((ib + 15) & ~(size_t)15));
   const size_t lds = pbuf + (size_t)(kThreads + 1 + sh.num_seqs + 1) * sizeof(int);
   const long long ml = max_seq_len > 0 ? max_seq_len : 1;
   const long long units_bound =

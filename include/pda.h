@@ -182,11 +182,11 @@ int validate_page_tags(const uint32_t* page_tags, int32_t num_pages,
  * paged_decode_attn for `shape` when no sequence is longer than
  * max_seq_len tokens. Vector-ALU path: a header plus one split-K partial
  * (G rows of Dv fp32 accumulators, a running max and a running sum per row)
- * per (sequence, chunk slot, kv head), the chunk count of a sequence rounded
- * up to a multiple of four; a smaller workspace down to the size for
- * max_seq_len = 1 is still accepted, and the device then widens the split
- * chunk (by doubling) until the partials fit, which changes results only
- * within rounding. Latent path: a header plus one partial (Hq rows of Dv + 4
+ * per (sequence, unit of up to four consecutive chunks, kv head), i.e. the
+ * chunk count of a sequence divided by four and rounded up; a smaller
+ * workspace down to one partial per (sequence, kv head) is still accepted,
+ * and the device then widens the split chunk (by doubling) until the
+ * partials fit, which changes results only within rounding. Latent path: a header plus one partial (Hq rows of Dv + 4
  * fp32) per (compute unit + sequence) of the current device; with less room
  * fewer workgroups are launched (at least one partial per sequence plus one
  * is required). Returns 0 for an invalid shape.

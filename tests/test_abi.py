@@ -59,10 +59,13 @@ def _shape(pda, **kw):
 
 
 def test_workspace_sizes(pda):
-    # 64 seqs x 16 chunks of 512 x 8 kv heads, each 8 rows x (128 + 2) fp32,
-    # after a 256-byte-aligned header of (64 + 65) ints
+    # 64 seqs x 4 units (of four 512-token chunks) x 8 kv heads, each
+    # partial 8 rows x (128 + 2) fp32, after a 256-byte-aligned header of
+    # (64 + 65) ints
     sh = _shape(pda)
-    assert pda.paged_decode_attn_workspace_bytes(sh, 8192) == 768 + 64 * 16 * 8 * 8 * 130 * 4
+    assert pda.paged_decode_attn_workspace_bytes(sh, 8192) == 768 + 64 * 4 * 8 * 8 * 130 * 4
+    # a ragged chunk count rounds up to whole units: 8193 tokens = 17 chunks
+    assert pda.paged_decode_attn_workspace_bytes(sh, 8193) == 768 + 64 * 5 * 8 * 8 * 130 * 4
     # invalid shapes give 0
     for bad in (dict(num_q_heads=60), dict(num_kv_heads=0), dict(page_size=0),
                 dict(split_tokens=100), dict(kv_dtype=7), dict(sm_scale=float("nan"))):

@@ -225,9 +225,9 @@ def test_small_workspace_widens_chunks(gpu):
     ref = oracle_attn(pr, kc, vc, ts)
     g = GpuProblem(gpu, pr)
     full = g.attend(split=64)
-    # room for one unit of four chunk slots per (sequence, kv head) only
+    # room for one unit partial per (sequence, kv head) only
     hdr = 256 * (-(-((64 + 3 + 1) * 4) // 256))
-    minimal = hdr + 3 * 2 * 4 * 8 * 130 * 4
+    minimal = hdr + 3 * 2 * 8 * 130 * 4
     tight = g.attend(split=64, ws_bytes=minimal)
     assert_attn_close(full, ref, "full workspace")
     assert_attn_close(tight, ref, "minimal workspace")
