@@ -245,6 +245,54 @@ __device__ __forceinline__ void settle_acc(float (&acc)[G][2]) {
   }
 }
 
+// One step of a full-wave max for every row: x[r] = max(x[r], x[r] of the
+// lane the DPP control names), fused as v_max_f32_dpp (the compiler would
+// emit a mov_dpp, a canonicalising max and a max). Rows are interleaved, so a
+// step's source was written G instructions before; for G < 3 the caller pads.
+template <int C, int G>
+__device__ __forceinline__ void max_step(float (&x)[G]) {
+#pragma unroll
+  for (int r = 0; r < G; ++r) {
+    if constexpr (C == 0)
+      asm volatile("v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+                   : "+v"(x[r]));
+    else if constexpr (C == 1)
+      asm volatile("v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+                   : "+v"(x[r]));
+    else if constexpr (C == 2)
+      asm volatile("v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf"
+                   : "+v"(x[r]));
+    else if constexpr (C == 3)
+      asm volatile("v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf"
+                   : "+v"(x[r]));
+    else if constexpr (C == 4)
+      asm volatile("v_max_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf"
+                   : "+v"(x[r]));
+    else
+      asm volatile("v_max_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf"
+                   : "+v"(x[r]));
+  }
+}
+
+// Full-wave maxima of G rows at once, as wave-uniform values: after the six
+// steps lane 63 holds each row's maximum (the row broadcasts only write the
+// rows their masks name; the others keep their values). Wait states: two
+// before the first DPP read of values the compiler just wrote, two between
+// steps when fewer than three rows separate a write from its DPP read, and
+// two before the lane reads, since the compiler pads nothing around inline
+// asm. NaN inputs are ignored unless a whole row is NaN (IEEE maximum).
+template <int G>
+__device__ __forceinline__ void wave_max_rows(float (&x)[G], float (&out)[G]) {
+  settle_rows<1>(x);
+  static_for<0, 6>::run([&](auto C) {
+    if constexpr (decltype(C)::value > 0 && G < 3) settle_rows<1>(x);
+    max_step<decltype(C)::value>(x);
+  });
+  settle_rows<1>(x);
+#pragma unroll
+  for (int r = 0; r < G; ++r) out[r] = as_f32(__builtin_amdgcn_readlane((int)as_u32(x[r]), 63));
+}
+
 // acc + dot(q, k) over one bf16 pair, where q is taken from lane L of the
 // lane's 16-lane row (DPP row_newbcast). Written as inline asm because the
 // compiler does not fold the broadcast into v_dot2c. The q register is only
@@ -700,8 +748,19 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
     // ---- online softmax (log2 units) -----------------------------------
     // zl = z*kmul - m. The running max m only moves when some score of the
     // block exceeds it by more than kTau, so p = 2^zl <= 2^kTau and the
-    // exact block maximum (a wave reduction) is only taken in that case.
+    // exact block maximum (a wave reduction) is only taken in that case. On
+    // the item's first block (m = -inf, l = acc = 0) every row's maximum is
+    // taken up front, all rows in one interleaved reduction, so no row
+    // takes the one-row path there.
     const bool tok_ok = (b0 + lane) < tok1;
+    if (b0 == tok0) {
+      float t[G], bm[G];
+#pragma unroll
+      for (int r = 0; r < G; ++r) t[r] = (tail && !tok_ok) ? -INFINITY : z[r] * kmul;
+      wave_max_rows<G>(t, bm);
+#pragma unroll
+      for (int r = 0; r < G; ++r) m[r] = bm[r];
+    }
     float zl[G];
     uint64_t over = 0;
 #pragma unroll

@@ -1,11 +1,13 @@
 """The attention kernel issues its DPP dot products (v_dot2c_f32_{bf16,f16}
-with a row broadcast) as inline asm, and the compiler does not insert the
-wait states such instructions need around code it cannot see into. This
-test compiles the kernel source to gfx950 assembly and checks every such
-instruction against the rules the source relies on:
+with a row broadcast) and the steps of its all-rows wave maximum
+(v_max_f32_dpp) as inline asm, and the compiler does not insert the wait
+states such instructions need around code it cannot see into. This test
+compiles the kernel source to gfx950 assembly and checks every DPP
+instruction (the compiler's own included) against the rules the source
+relies on:
 
-  * no VGPR the DPP dot reads as its broadcast source or second operand was
-    written by a VALU instruction in the two wait states before it;
+  * no VGPR a DPP instruction reads was written by a VALU instruction in the
+    two wait states before it;
   * a dot's result is not read by any other instruction within three wait
     states, except by the next dot of the same kind as its accumulator.
 
@@ -47,6 +49,7 @@ def _violations(asm):
             if not op.startswith("v_"):
                 continue
             is_dot = op.startswith("v_dot2c_") and op.endswith("_dpp")
+            is_dpp = op.endswith("_dpp")
             srcs = set()
             for o in ops[1:]:
                 srcs |= _regs(o)
@@ -61,7 +64,7 @@ def _violations(asm):
                 if pop.startswith("v_") and pops:
                     pdst = _regs(pops[0])
                     prev_dot = pop.startswith("v_dot2c_") and pop.endswith("_dpp")
-                    if is_dot and ws < 2 and (srcs & pdst):
+                    if is_dpp and ws < 2 and (srcs & pdst):
                         bad.append(("VALU write -> DPP source", ins[j], line))
                     if prev_dot and pdst:
                         reads = srcs | (dst if is_dot else set())
@@ -84,5 +87,6 @@ def test_dpp_dot_wait_states(tmp_path):
     asm = out.read_text()
     n = len(re.findall(r"v_dot2c_f32_\w+_dpp", asm))
     assert n > 0, "no DPP dot products found"
+    assert re.search(r"v_max_f32_dpp", asm), "no fused DPP maximum found"
     bad = _violations(asm)
     assert not bad, f"{len(bad)} wait-state violations, first: {bad[:3]}"
