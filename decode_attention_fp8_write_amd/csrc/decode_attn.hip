@@ -364,26 +364,36 @@ __device__ __forceinline__ void load_k(const AttnArgs& a, int g, const Pages& pg
 // address + 16 i), laid out [column group c][token][16 codes]: one 1 KB copy
 // per column group, and a token's 16 codes at kw + c*1024 + 16*token, so the
 // QK reads (lane = token) are conflict-free. No registers hold keys in flight.
+// Source of the lane's token (column group 0) for a block's key copy.
 template <int S>
-__device__ __forceinline__ void dma_k(const AttnArgs& a, int g, const Pages& pg, uint8_t* kw) {
+__device__ __forceinline__ const uint8_t* k_src(const AttnArgs& a, int g, const Pages& pg) {
   const int lane = __lane_id();
   int page = pg.p0;
   if constexpr (S <= 32) page += (lane >= S) * (pg.p1 - pg.p0);
   if constexpr (S == 16) page += (lane >= 2 * S) * (pg.p2 - pg.p1) + (lane >= 3 * S) * (pg.p3 - pg.p2);
   const int off = lane % S;
-  const uint8_t* src = a.kc + ((((int64_t)page * a.Hkv + g) * 8) * S + off) * 16;
-  // Issued as inline asm so that the compiler's wait-count bookkeeping does
-  // not treat every later LDS read as dependent on it (it would wait for all
-  // vector-memory operations, including the next block's V loads); the one
-  // reader, the QK of the next block, waits for it explicitly.
+  return a.kc + ((((int64_t)page * a.Hkv + g) * 8) * S + off) * 16;
+}
+
+// Copy of column group c of a block's keys into the wave's buffer. Issued
+// as inline asm so that the compiler's wait-count bookkeeping does not treat
+// every later LDS read as dependent on it (it would wait for all
+// vector-memory operations, including the next block's V loads); the one
+// reader, the QK of the next block, waits for it explicitly.
+template <int S>
+__device__ __forceinline__ void dma_k_group(const uint8_t* src, uint8_t* kw, int c) {
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)kw));
+  const uint8_t* gp = src + (int64_t)c * S * 16;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds0 + c * 1024), "v"(gp) : "memory");
+}
+
+template <int S>
+__device__ __forceinline__ void dma_k(const AttnArgs& a, int g, const Pages& pg, uint8_t* kw) {
+  const uint8_t* src = k_src<S>(a, g, pg);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint8_t* gp = src + (int64_t)c * S * 16;
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(lds0 + c * 1024), "v"(gp) : "memory");
-  }
+  for (int c = 0; c < 8; ++c) dma_k_group<S>(src, kw, c);
 }
 
 // V of one 64-token block for the lane's two dims (2*lane, 2*lane+1): one
@@ -668,6 +678,9 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
       uint4 kcur = readk(0), knext = kcur;
       uint4 qcur = readq(0), qnext = qcur;
       bf16x2_t kp[8];
+      // the next block's key copy goes out group by group, each group as
+      // soon as its keys here have been read and used
+      const uint8_t* ksrc = has_next ? k_src<S>(a, g, npg) : nullptr;
       settle_rows<1>(z);
       static_for<0, 8>::run([&](auto C) {
         constexpr int c16 = decltype(C)::value;
@@ -693,10 +706,11 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
           z[d / 8] = dot2_bcast<d / 4>(z[d / 8], u4_get(qv, d % 4), kp[d % 8]);
         });
         __builtin_amdgcn_sched_barrier(0);
+        // group c16's keys are in registers (converted above): its part of
+        // the buffer is free
+        if (has_next) dma_k_group<S>(ksrc, kw, c16);
       });
       settle_rows<2>(z);
-      // every key read of this block has been consumed: the buffer is free
-      if (has_next) dma_k<S>(a, g, npg, kw);
     } else {
     // Eight dims (four q pairs per row) at a time, q in SGPRs. The loads of
     // chunk c+2 are released by a fence that consumes the scores produced by
