@@ -1269,7 +1269,12 @@ extern "C" int paged_decode_attn(const pda_attn_shape* shape, const void* q, con
   const long long ml = max_seq_len > 0 ? max_seq_len : 1;
   const long long units_bound =
       (long long)sh.num_seqs * sh.num_kv_heads * (((ml + chunk - 1) / chunk + kWaves - 1) / kWaves);
-  long long grid = (long long)device_cu_count() * blocks_per_cu(pk, lds);
+  // Four times the resident workgroups (each takes units round-robin): the
+  // dispatcher starts workgroups as others retire, so the workgroups sharing
+  // a CU reach their unit boundaries (barriers, first loads of an item) at
+  // different times instead of all at once; more would mostly add workgroups
+  // that find no unit when many sequences are short.
+  long long grid = (long long)device_cu_count() * blocks_per_cu(pk, lds) * 4;
   if (grid > units_bound) grid = units_bound;
   if (grid < 1) grid = 1;
   hipStream_t s = as_stream(stream);
