@@ -120,29 +120,34 @@ __device__ int build_plan(const AttnArgs& a, int S, int* pref, int* tmp, int& ch
   const int per = (a.B + kThreads - 1) / kThreads;
   const int beg = min(a.B, tid * per);
   const int end = min(a.B, beg + per);
+  const int lane = tid & 63, wave = tid >> 6;
   int chunk = a.chunk0;
   int total = 0;
   for (;;) {
     int local = 0;
     for (int s = beg; s < end; ++s) local += n_slots_of(a, s, S, chunk);
-    tmp[tid] = local;
-    __syncthreads();
-    if (tid == 0) {
-      int run = 0;
-      for (int i = 0; i < kThreads; ++i) {
-        const int v = tmp[i];
-        tmp[i] = run;
-        run += v;
-      }
-      tmp[kThreads] = run;
+    // exclusive prefix of `local` over the workgroup: an inclusive scan
+    // within each wave, then the totals of the waves before this one
+    int v = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(v, o);
+      if (lane >= o) v += t;
     }
+    if (lane == 63) tmp[wave] = v;
     __syncthreads();
-    int run = tmp[tid];
+    int run = v - local;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int t = tmp[w];
+      if (w < wave) run += t;
+      total += t;
+    }
     for (int s = beg; s < end; ++s) {
       pref[s] = run;
       run += n_slots_of(a, s, S, chunk);
     }
-    total = tmp[kThreads];
     __syncthreads();
     if ((long long)(total / kWaves) * a.Hkv <= a.cap_items) break;
     chunk *= 2;
@@ -230,18 +235,27 @@ __device__ __forceinline__ void settle_rows(float (&z)[R]) {
 }
 template <int N, int G>
 __device__ __forceinline__ void settle_acc(float (&acc)[G][2]) {
-  float a0[G], a1[G];
-#pragma unroll
-  for (int r = 0; r < G; ++r) {
-    a0[r] = acc[r][0];
-    a1[r] = acc[r][1];
-  }
-  settle_rows<N>(a0);
-  settle_rows<N>(a1);
-#pragma unroll
-  for (int r = 0; r < G; ++r) {
-    acc[r][0] = a0[r];
-    acc[r][1] = a1[r];
+  // the accumulators themselves are the operands (a copy through another
+  // array made the register allocator move them on every block)
+  if constexpr (G == 1) {
+    asm volatile("s_nop %2" : "+v"(acc[0][0]), "+v"(acc[0][1]) : "n"(N));
+  } else if constexpr (G == 2) {
+    asm volatile("s_nop %4"
+                 : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1])
+                 : "n"(N));
+  } else if constexpr (G == 4) {
+    asm volatile("s_nop %8"
+                 : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]),
+                   "+v"(acc[2][0]), "+v"(acc[2][1]), "+v"(acc[3][0]), "+v"(acc[3][1])
+                 : "n"(N));
+  } else {
+    static_assert(G == 8, "G in {1, 2, 4, 8}");
+    asm volatile("s_nop %16"
+                 : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]),
+                   "+v"(acc[2][0]), "+v"(acc[2][1]), "+v"(acc[3][0]), "+v"(acc[3][1]),
+                   "+v"(acc[4][0]), "+v"(acc[4][1]), "+v"(acc[5][0]), "+v"(acc[5][1]),
+                   "+v"(acc[6][0]), "+v"(acc[6][1]), "+v"(acc[7][0]), "+v"(acc[7][1])
+                 : "n"(N));
   }
 }
 
@@ -558,9 +572,17 @@ __device__ __forceinline__ void pv_block(
   });
 }
 
-template <int G, bool FP8, int S>
+template <int G, bool FP8, int S, typename QStore>
 __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, uint16_t* pw,
-                             uint8_t* kw, const uint32_t* qs, float* mg) {
+                             uint8_t* kw, const uint32_t* qs, float* mg, bool active,
+                             QStore&& q_store) {
+  // q_store (the unit's q rows into LDS, then a workgroup barrier) runs in
+  // every wave, after an active wave has issued its first block's loads, so
+  // that their latency and the q loads' overlap.
+  if (!active) {
+    q_store();
+    return;
+  }
   using I = Item<G, FP8, S>;
   using W = typename I::vword_t;
   constexpr int NP = I::NP;
@@ -642,6 +664,7 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
   else
     load_k<G, FP8, S>(a, g, pg, kk);
   load_v<G, FP8, S>(a, g, pg, vv);
+  q_store();
 
   for (;;) {
     const int bn = b0 + 64;
@@ -956,19 +979,34 @@ void attn_partial_kernel(AttnArgs a) {
     const int j = local % ncq;   // unit of (s, g)
     const int c = __builtin_amdgcn_readfirstlane(j * kWaves + wave);
     __syncthreads();   // the previous unit's reads of qs and the merge slots are done
+    // q rows of (s, g) (FP8) into LDS as [column group c16][row r][8
+    // dwords], so the 8G dwords one QK step of 16 dims needs are contiguous.
+    // The loads are issued here, before the item's first loads; the stores
+    // and the barrier come after those (in process_item).
+    constexpr int QPT = FP8 ? (G * kD / 2 + kThreads - 1) / kThreads : 1;   // dwords per thread
+    uint32_t qreg[QPT];
+    const uint32_t* qg =
+        reinterpret_cast<const uint32_t*>(a.q + ((int64_t)s * a.Hq + (int64_t)g * G) * kD);
     if constexpr (FP8) {
-      // q rows of (s, g) into LDS as [column group c16][row r][8 dwords]:
-      // the 8G dwords one QK step of 16 dims needs are contiguous
-      const uint32_t* qg =
-          reinterpret_cast<const uint32_t*>(a.q + ((int64_t)s * a.Hq + (int64_t)g * G) * kD);
-      for (int i = threadIdx.x; i < G * kD / 2; i += kThreads) {
-        const int r = i / (kD / 2), w = i % (kD / 2);   // row, dword of the row
-        qs[((w / 8) * G + r) * 8 + (w % 8)] = qg[i];
+#pragma unroll
+      for (int k = 0; k < QPT; ++k) {
+        const int i = threadIdx.x + k * kThreads;
+        if (i < G * kD / 2) qreg[k] = qg[i];
       }
-      __syncthreads();
     }
+    auto q_store = [&]() {
+      if constexpr (FP8) {
+#pragma unroll
+        for (int k = 0; k < QPT; ++k) {
+          const int i = threadIdx.x + k * kThreads;
+          const int r = i / (kD / 2), w = i % (kD / 2);   // row, dword of the row
+          if (i < G * kD / 2) qs[((w / 8) * G + r) * 8 + (w % 8)] = qreg[k];
+        }
+        __syncthreads();
+      }
+    };
     const int nch = n_chunks_of(a, s, S, chunk);
-    if (c < nch) process_item<G, FP8, S>(a, s, c, g, chunk, pw, kw, qs, mg0 + wave * MS);
+    process_item<G, FP8, S>(a, s, c, g, chunk, pw, kw, qs, mg0 + wave * MS, c < nch, q_store);
     __syncthreads();
     float* part = a.ws_part + ((int64_t)(pref[s] / kWaves + j) * a.Hkv + g) * (G * (kD + 2));
     merge_unit<G>(mg0, MS, min(kWaves, nch - j * kWaves), part);
