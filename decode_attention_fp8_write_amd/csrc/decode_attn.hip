@@ -259,48 +259,51 @@ __device__ __forceinline__ void settle_acc(float (&acc)[G][2]) {
   }
 }
 
-// One step of a full-wave max for every row: x[r] = max(x[r], x[r] of the
-// lane the DPP control names), fused as v_max_f32_dpp (the compiler would
-// emit a mov_dpp, a canonicalising max and a max). Rows are interleaved, so a
-// step's source was written G instructions before; for G < 3 the caller pads.
-template <int C, int G>
-__device__ __forceinline__ void max_step(float (&x)[G]) {
+// One step of a full-wave reduction for every row: x[r] = op(x[r], x[r] of
+// the lane the DPP control names), fused as v_max_f32_dpp / v_add_f32_dpp
+// (the compiler would emit a mov_dpp, for the maximum a canonicalising max,
+// and the operation). Rows are interleaved, so a step's source was written
+// G instructions before; for G < 3 the caller pads.
+#define PDA_DPP_STEP(OP, CTRL) \
+  asm volatile(OP " %0, %0, %0 " CTRL " bank_mask:0xf" : "+v"(x[r]))
+template <bool ADD, int C, int G>
+__device__ __forceinline__ void reduce_step(float (&x)[G]) {
 #pragma unroll
   for (int r = 0; r < G; ++r) {
-    if constexpr (C == 0)
-      asm volatile("v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
-                   : "+v"(x[r]));
-    else if constexpr (C == 1)
-      asm volatile("v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
-                   : "+v"(x[r]));
-    else if constexpr (C == 2)
-      asm volatile("v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf"
-                   : "+v"(x[r]));
-    else if constexpr (C == 3)
-      asm volatile("v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf"
-                   : "+v"(x[r]));
-    else if constexpr (C == 4)
-      asm volatile("v_max_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf"
-                   : "+v"(x[r]));
-    else
-      asm volatile("v_max_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf"
-                   : "+v"(x[r]));
+    if constexpr (ADD) {
+      if constexpr (C == 0) PDA_DPP_STEP("v_add_f32_dpp", "quad_perm:[1,0,3,2] row_mask:0xf");
+      else if constexpr (C == 1) PDA_DPP_STEP("v_add_f32_dpp", "quad_perm:[2,3,0,1] row_mask:0xf");
+      else if constexpr (C == 2) PDA_DPP_STEP("v_add_f32_dpp", "row_half_mirror row_mask:0xf");
+      else if constexpr (C == 3) PDA_DPP_STEP("v_add_f32_dpp", "row_mirror row_mask:0xf");
+      else if constexpr (C == 4) PDA_DPP_STEP("v_add_f32_dpp", "row_bcast:15 row_mask:0xa");
+      else PDA_DPP_STEP("v_add_f32_dpp", "row_bcast:31 row_mask:0xc");
+    } else {
+      if constexpr (C == 0) PDA_DPP_STEP("v_max_f32_dpp", "quad_perm:[1,0,3,2] row_mask:0xf");
+      else if constexpr (C == 1) PDA_DPP_STEP("v_max_f32_dpp", "quad_perm:[2,3,0,1] row_mask:0xf");
+      else if constexpr (C == 2) PDA_DPP_STEP("v_max_f32_dpp", "row_half_mirror row_mask:0xf");
+      else if constexpr (C == 3) PDA_DPP_STEP("v_max_f32_dpp", "row_mirror row_mask:0xf");
+      else if constexpr (C == 4) PDA_DPP_STEP("v_max_f32_dpp", "row_bcast:15 row_mask:0xa");
+      else PDA_DPP_STEP("v_max_f32_dpp", "row_bcast:31 row_mask:0xc");
+    }
   }
 }
+#undef PDA_DPP_STEP
 
-// Full-wave maxima of G rows at once, as wave-uniform values: after the six
-// steps lane 63 holds each row's maximum (the row broadcasts only write the
-// rows their masks name; the others keep their values). Wait states: two
-// before the first DPP read of values the compiler just wrote, two between
-// steps when fewer than three rows separate a write from its DPP read, and
-// two before the lane reads, since the compiler pads nothing around inline
-// asm. NaN inputs are ignored unless a whole row is NaN (IEEE maximum).
-template <int G>
-__device__ __forceinline__ void wave_max_rows(float (&x)[G], float (&out)[G]) {
+// Full-wave maxima (ADD = false) or sums (ADD = true) of G rows at once, as
+// wave-uniform values: after the six steps lane 63 holds each row's result
+// (the row broadcasts only write the rows their masks name; the others keep
+// their values), pairing lanes in the same order as the one-row reductions.
+// Wait states: two before the first DPP read of values the compiler just
+// wrote, two between steps when fewer than three rows separate a write from
+// its DPP read, and two before the lane reads, since the compiler pads
+// nothing around inline asm. A maximum ignores NaN inputs unless a whole row
+// is NaN (IEEE maximum).
+template <bool ADD, int G>
+__device__ __forceinline__ void wave_reduce_rows(float (&x)[G], float (&out)[G]) {
   settle_rows<1>(x);
   static_for<0, 6>::run([&](auto C) {
     if constexpr (decltype(C)::value > 0 && G < 3) settle_rows<1>(x);
-    max_step<decltype(C)::value>(x);
+    reduce_step<ADD, decltype(C)::value>(x);
   });
   settle_rows<1>(x);
 #pragma unroll
@@ -794,7 +797,7 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
       float t[G], bm[G];
 #pragma unroll
       for (int r = 0; r < G; ++r) t[r] = (tail && !tok_ok) ? -INFINITY : z[r] * kmul;
-      wave_max_rows<G>(t, bm);
+      wave_reduce_rows<false, G>(t, bm);
 #pragma unroll
       for (int r = 0; r < G; ++r) m[r] = bm[r];
     }
@@ -873,13 +876,14 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
   // [G rows x 128 dims][G maxima][G sums]; a bad item's maxima are NaN.
   // (For FP8 the slot is the key buffer, whose last copy was waited for
   // before the last QK.)
+  float lt[G];
+  wave_reduce_rows<true, G>(l, lt);   // l is not used after this
 #pragma unroll
   for (int r = 0; r < G; ++r) {
-    const float lt = wave_sum(l[r]);
     *reinterpret_cast<float2*>(mg + r * kD + 2 * lane) = make_float2(acc[r][0], acc[r][1]);
     if (lane == r) {
       mg[G * kD + r] = bad ? __builtin_nanf("") : m[r];
-      mg[G * kD + G + r] = lt;
+      mg[G * kD + G + r] = lt[r];
     }
   }
 }
