@@ -298,34 +298,33 @@ void latent_partial_kernel(LatArgs a) {
       // hoisting every read and conversion (a register each).
       f32x16_t st[2] = {f32x16_t{}, f32x16_t{}};
       {
+        // reads run two steps ahead: a step converts its codes, then reuses
+        // their registers for the read two steps on, then issues its MFMAs
         const uint8_t* rowp = pb.codes + n * 16 + 8 * h;
-        uint2 cur0 = *reinterpret_cast<const uint2*>(rowp);
-        uint2 cur1 = *reinterpret_cast<const uint2*>(rowp + 32 * 16);
+        auto rdk = [&](int k, int t) -> uint2 {
+          return *reinterpret_cast<const uint2*>(rowp + k * (kS * 16) + t * (32 * 16));
+        };
+        uint2 ra[2] = {rdk(0, 0), rdk(1, 0)};
+        uint2 rb[2] = {rdk(0, 1), rdk(1, 1)};
         sfor<0, kGroups>::run([&](auto K) {
           constexpr int k = decltype(K)::value;
-          uint2 nx0 = cur0, nx1 = cur1;
-          if constexpr (k + 1 < kGroups) {
-            nx0 = *reinterpret_cast<const uint2*>(rowp + (k + 1) * (kS * 16));
-            nx1 = *reinterpret_cast<const uint2*>(rowp + (k + 1) * (kS * 16) + 32 * 16);
+          const uint2 c0 = ra[k & 1], c1 = rb[k & 1];
+          const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0.x, 1.0f, false);
+          const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0.x, 1.0f, true);
+          const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0.y, 1.0f, false);
+          const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0.y, 1.0f, true);
+          const bf16x2_t u0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1.x, 1.0f, false);
+          const bf16x2_t u1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1.x, 1.0f, true);
+          const bf16x2_t u2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1.y, 1.0f, false);
+          const bf16x2_t u3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1.y, 1.0f, true);
+          if constexpr (k + 2 < kGroups) {
+            ra[k & 1] = rdk(k + 2, 0);
+            rb[k & 1] = rdk(k + 2, 1);
           }
-          {
-            const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur0.x, 1.0f, false);
-            const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur0.x, 1.0f, true);
-            const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur0.y, 1.0f, false);
-            const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur0.y, 1.0f, true);
-            const bf16x8_t av = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-            st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[k], st[0], 0, 0, 0);
-          }
-          {
-            const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur1.x, 1.0f, false);
-            const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur1.x, 1.0f, true);
-            const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur1.y, 1.0f, false);
-            const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cur1.y, 1.0f, true);
-            const bf16x8_t av = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-            st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[k], st[1], 0, 0, 0);
-          }
-          cur0 = nx0;
-          cur1 = nx1;
+          const bf16x8_t a0 = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+          const bf16x8_t a1 = {u0.x, u0.y, u1.x, u1.y, u2.x, u2.y, u3.x, u3.y};
+          st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[k], st[0], 0, 0, 0);
+          st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[k], st[1], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         });
       }
@@ -403,20 +402,21 @@ void latent_partial_kernel(LatArgs a) {
               (__attribute__((address_space(3))) i32x2_t*)(vbase + 16 * ks * 16 +
                                                            2 * d * (kS * 16)));
         };
-        i32x2_t cw = rd(0, 0);
-        sfor<0, 4 * (kDv / 32)>::run([&](auto I) {
-          constexpr int ks = decltype(I)::value / (kDv / 32);
-          constexpr int d = decltype(I)::value % (kDv / 32);
-          i32x2_t nx = cw;
-          if constexpr (d + 1 < kDv / 32) nx = rd(ks, d + 1);
-          else if constexpr (ks + 1 < 4) nx = rd(ks + 1, 0);
+        // reads run two steps ahead (step I = ks * 16 + d), as in QK
+        constexpr int kPV = 4 * (kDv / 32);
+        i32x2_t rr[2] = {rd(0, 0), rd(0, 1)};
+        sfor<0, kPV>::run([&](auto I) {
+          constexpr int i = decltype(I)::value;
+          constexpr int ks = i / (kDv / 32);
+          constexpr int d = i % (kDv / 32);
+          const i32x2_t cw = rr[i & 1];
           const f16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)cw.x, 1.0f, false);
           const f16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)cw.x, 1.0f, true);
           const f16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)cw.y, 1.0f, false);
           const f16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)cw.y, 1.0f, true);
+          if constexpr (i + 2 < kPV) rr[i & 1] = rd((i + 2) / (kDv / 32), (i + 2) % (kDv / 32));
           const f16x8_t av = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y, v3.x, v3.y};
           acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pk[ks], acc[d], 0, 0, 0);
-          cw = nx;
           __builtin_amdgcn_sched_barrier(0);
         });
       }
