@@ -30,7 +30,12 @@ def build(save_temps: str | None = None, verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Wall", "-Wno-unused-function", *DEVICE_FLAGS, "-I", INCLUDE, "-I", CSRC,
+           "-Wall", "-Wno-unused-function",
+           # a pointer squeezed through a 32-bit value (e.g. a lane broadcast
+           # builtin that takes int) is an address fault on the GPU: refuse it
+           "-Werror=int-to-pointer-cast", "-Werror=pointer-to-int-cast",
+           "-Werror=shorten-64-to-32",
+           *DEVICE_FLAGS, "-I", INCLUDE, "-I", CSRC,
            "-o", tmp, *sources()]
     cwd = None
     if save_temps:

@@ -252,12 +252,26 @@ void latent_partial_kernel(LatArgs a) {
       // of the page loop (all vector memory, then a barrier) covers it.
       const uint32_t l0 = __builtin_amdgcn_readfirstlane(
           (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)pb.codes));
+      // The page base is wave-uniform: each copy takes an SGPR base (page +
+      // i KB, scalar arithmetic) and the one per-lane offset lane * 16, so no
+      // per-copy lane address is kept in (or spilled from) vector registers;
+      // a spilled one would be reloaded, and waited for, before every copy.
+      // (readfirstlane takes and returns 32 bits: each half separately)
+      const uint64_t s64 = (uint64_t)(uintptr_t)src;
+      const uint32_t s_lo = __builtin_amdgcn_readfirstlane((uint32_t)s64);
+      const uint32_t s_hi = __builtin_amdgcn_readfirstlane((uint32_t)(s64 >> 32));
+      const uint8_t* srcu = (const uint8_t*)(uintptr_t)(((uint64_t)s_hi << 32) | s_lo);
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
+      // recomputed here (opaque to the compiler, three VALU instructions)
+      // rather than kept live across the page and spilled
+      uint32_t lane16;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0\n\t"
+                   "v_lshlrev_b32 %0, 4, %0" : "=v"(lane16));
 #pragma unroll
       for (int ii = 0; ii < kWaveChunks / NW; ++ii) {
-        const int i = ii * NW + wave;
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                     :: "s"(__builtin_amdgcn_readfirstlane(l0 + i * 1024)),
-                        "v"(src + (i * 64 + lane) * 16)
+        const int i = ii * NW + wv;
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :: "s"(l0 + (uint32_t)i * 1024u), "v"(lane16), "s"(srcu + (int64_t)i * 1024)
                      : "memory");
       }
       if (tid < kS) sc_next = a.tscale[(int64_t)page * kS + tid];
