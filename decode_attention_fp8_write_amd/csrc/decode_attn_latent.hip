@@ -19,9 +19,10 @@
 // fragments of each sequence with a log-sum-exp rule.
 //
 // Inside a fragment, one page (64 tokens) at a time:
-//  * the workgroup copies the page's 36 KB of codes and its 64 scales into
-//    LDS (double-buffered: the next page is fetched into registers while the
-//    current one is computed). Tokens past the end are written as zero codes
+//  * the workgroup copies the page's 36 KB of codes into LDS by direct
+//    global->LDS copies, and its 64 scales (double-buffered: the next page's
+//    copy is issued as soon as the page's barrier is passed and runs while
+//    the current one is computed). Tokens past the end are written as zero codes
 //    with weight 0, so they contribute nothing and poisoned bytes are never
 //    read into the arithmetic.
 //  * wave w owns query heads [32w, 32w+32). QK as S^T = K Q^T on
@@ -279,7 +280,7 @@ void latent_partial_kernel(LatArgs a) {
     // After the copy of page j has landed: zero the codes of tokens past the
     // end (they then add nothing, whatever the slot held) and fill the
     // per-token arrays.
-    auto finish = [&](int j, PageBuf& pb) {
+    auto finish = [&](int j, PageBuf& pb, float sc) {
       const int valid = min(kS, len - j * kS);   // tokens of this page in use
       if (valid < kS) {
         for (int c = tid; c < kPageBytes / 16; c += NT)
@@ -288,9 +289,9 @@ void latent_partial_kernel(LatArgs a) {
       if (tid < kS) {
         // v_log_f32 is log2
         const bool live = tid < valid;
-        pb.a[tid] = live ? sc_next * c0 : 0.0f;
-        pb.b[tid] = live ? __builtin_amdgcn_logf(sc_next) : -INFINITY;
-        pb.inv[tid] = live ? 1.0f / sc_next : 0.0f;
+        pb.a[tid] = live ? sc * c0 : 0.0f;
+        pb.b[tid] = live ? __builtin_amdgcn_logf(sc) : -INFINITY;
+        pb.inv[tid] = live ? 1.0f / sc : 0.0f;
       }
     };
 
@@ -300,15 +301,18 @@ void latent_partial_kernel(LatArgs a) {
       // page j's copy (and every earlier load) complete, then publish
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      finish(j, pb);
-      __syncthreads();
-      // the other buffer's last readers passed the barriers above
+      // The next page's copy goes out first: the other buffer's last readers
+      // (page j - 1) passed the barrier above. Page j's scales came with its
+      // copy; keep them before the next copy's scale load replaces them.
+      const float sc_cur = sc_next;
       if (j + 1 < j1) fetch(j + 1, buf[(j + 1 - j0) & 1]);
+      finish(j, pb, sc_cur);
+      __syncthreads();
 
       // ---- QK: S^T (64 tokens x 32 heads) as two 32x32 tiles --------------
       // A operand of k-step k, tile t: lane (token 32t + n, half h) holds the
-      // codes of dims 16k + 8h .. +7 (8 bytes, one LDS read). Reads run one
-      // step ahead; the scheduling barrier per step keeps the compiler from
+      // codes of dims 16k + 8h .. +7 (8 bytes, one LDS read). Reads run two
+      // steps ahead; the scheduling barrier per step keeps the compiler from
       // hoisting every read and conversion (a register each).
       f32x16_t st[2] = {f32x16_t{}, f32x16_t{}};
       {
