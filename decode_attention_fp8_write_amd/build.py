@@ -18,7 +18,11 @@ LIB = os.path.join(PKG, "libpda.so")
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are switched off for every HIP source.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # matrix-core products the compiler places write VGPRs: the
+                # latent kernel's score tiles stay out of the AGPRs its inline-asm
+                # output accumulators fill
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def sources():

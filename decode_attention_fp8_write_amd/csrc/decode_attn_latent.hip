@@ -25,22 +25,29 @@
 //    the current one is computed). Tokens past the end are written as zero codes
 //    with weight 0, so they contribute nothing and poisoned bytes are never
 //    read into the arithmetic.
-//  * wave w owns query heads [32w, 32w+32). QK as S^T = K Q^T on
-//    v_mfma_f32_32x32x16_bf16: K codes convert exactly to bf16 (A operand,
-//    lane = token), Q stays resident in registers as bf16 (B operand, lane =
-//    head), so Q enters exactly.
+//  * wave w owns query heads [32w, 32w+32), as two tiles of 16. Every
+//    product runs on 16x16x32 matrix-core tiles, whose operand reads from
+//    the token-major page hit every LDS bank once per half-wave (a lane reads
+//    8 bytes; the 32 lanes of a half-wave cover 16 tokens' full 16-byte
+//    slots, whose tokens differ mod 16).
+//  * QK as S^T = K Q^T on v_mfma_f32_16x16x32_bf16: K codes convert exactly
+//    to bf16 (A operand, lane = token row), Q stays resident in registers as
+//    bf16 (B operand, lane = head), so Q enters exactly. Token tile t holds
+//    tokens 16t .. 16t+15; in odd tiles row m is token 16t + (m ^ 8), so
+//    that each half-wave of the PV transpose read below also meets 16
+//    distinct token residues.
 //  * softmax in log2 units with the per-token scale folded in: for token t
 //    with scale c_t, y = (q.code_t) * c_t * sm_scale * log2(e) + log2(c_t);
 //    p' = 2^(y - m) = c_t * e^(score - m'), so the weights already carry the
 //    value scale, and the running sum adds p' / c_t. The running max m only
 //    moves when a page's max exceeds it by more than 8 (p' <= 2^8).
-//  * PV as O^T = V^T P^T on v_mfma_f32_32x32x16_f16: V codes convert exactly
+//  * PV as O^T = V^T P^T on v_mfma_f32_16x16x32_f16: V codes convert exactly
 //    to f16. The A operand needs eight tokens of one dim per lane; the LDS
 //    transpose read ds_read_b64_tr_b8 gathers them from the token-major page
 //    (in each 16-lane group, lane i receives byte i%8 of the eight 8-byte
 //    chunks addressed by lanes 2b + i/8). P^T is the B operand straight from
-//    the QK accumulator registers: its token order fixes the order in which
-//    the transpose read gathers V.
+//    the QK accumulator registers (k-step kk takes token tiles 2kk, 2kk+1):
+//    their token order fixes the order in which the transpose read gathers V.
 #include <mutex>
 #include <type_traits>
 
@@ -52,7 +59,8 @@ namespace {
 constexpr int kDk = 576;            // latent key dims
 constexpr int kDv = 512;            // value dims (first 512 of the key)
 constexpr int kS = 64;              // page size
-constexpr int kGroups = kDk / 16;   // 16-dim column groups per token
+constexpr int kKSteps = kDk / 32;   // 32-dim QK k-steps per token
+constexpr int kDTiles = kDv / 16;   // 16-dim PV output tiles
 constexpr int kPageBytes = kDk * kS;
 constexpr int kHeadsPerWave = 32;
 constexpr int kMaxWaves = 4;
@@ -63,7 +71,12 @@ constexpr float kTauL = 8.0f;
 constexpr float kLog2eL = 1.4426950408889634f;
 constexpr int kHdrL = 64;           // header ints, then pref[B+1]
 constexpr int kRow = kDv + 4;       // partial row: Dv sums, max, sum, 2 pad (16-byte rows)
-constexpr int kMaxSeqsL = 8192;
+constexpr int kMaxSeqsL = 2048;
+// Q of k-steps [0, kQReg) stays in registers, the rest is read from LDS
+// (registers would spill otherwise; a spill reload waits on the memory
+// counter that also tracks the page copy in flight)
+constexpr int kQReg = 9;
+constexpr int kQLdsWave = (kKSteps - kQReg) * 2 * 64 * 16;   // bytes per wave
 
 template <int F, int L>
 struct sfor {
@@ -78,7 +91,7 @@ struct sfor {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
 struct LatArgs {
@@ -114,31 +127,28 @@ struct PageBuf {
   float a[kS];     // scale * sm_scale * log2 e   (0 for tokens past the end)
   float b[kS];     // log2(scale)                  (-inf past the end)
   float inv[kS];   // 1 / scale                    (0 past the end)
+  float sraw[kS];  // the page's scales as stored (copied with the codes)
 };
 
-// acc[d] *= alpha for the (rare) running-max move, through global memory:
-// store the accumulators (lane's head row, layout of the partial), wait, and
-// load them back scaled. The row belongs to this lane alone.
-__device__ __forceinline__ void rescale_via(float* row, f32x16_t (&acc)[kDv / 32], float alpha) {
-  const int h = __lane_id() >> 5;
+// acc *= alpha for the (rare) running-max move, through global memory:
+// store the accumulators (the lane's two head rows, layout of the partial),
+// wait, and load them back scaled. The rows belong to this lane alone.
+// acc[c][ht] register r: dim 16c + 4g + r of head 16 ht + n.
+__device__ __forceinline__ void rescale_via(float* row0, float* row1, f32x4_t (&acc)[kDTiles][2],
+                                            float alpha0, float alpha1) {
+  const int g = __lane_id() >> 4;
 #pragma unroll
-  for (int d = 0; d < kDv / 32; ++d)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4)
-      *reinterpret_cast<float4*>(row + 32 * d + r4 * 8 + 4 * h) =
-          make_float4(acc[d][4 * r4], acc[d][4 * r4 + 1], acc[d][4 * r4 + 2], acc[d][4 * r4 + 3]);
+  for (int c = 0; c < kDTiles; ++c) {
+    *reinterpret_cast<f32x4_t*>(row0 + 16 * c + 4 * g) = acc[c][0];
+    *reinterpret_cast<f32x4_t*>(row1 + 16 * c + 4 * g) = acc[c][1];
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
-  for (int d = 0; d < kDv / 32; ++d)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const float4 v = *reinterpret_cast<const float4*>(row + 32 * d + r4 * 8 + 4 * h);
-      acc[d][4 * r4] = v.x * alpha;
-      acc[d][4 * r4 + 1] = v.y * alpha;
-      acc[d][4 * r4 + 2] = v.z * alpha;
-      acc[d][4 * r4 + 3] = v.w * alpha;
-    }
+  for (int c = 0; c < kDTiles; ++c) {
+    acc[c][0] = *reinterpret_cast<const f32x4_t*>(row0 + 16 * c + 4 * g) * alpha0;
+    acc[c][1] = *reinterpret_cast<const f32x4_t*>(row1 + 16 * c + 4 * g) * alpha1;
+  }
 }
 
 template <int NW>
@@ -146,14 +156,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void latent_partial_kernel(LatArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   PageBuf* buf = reinterpret_cast<PageBuf*>(smem);                 // [2]
-  int* tmp = reinterpret_cast<int*>(smem + 2 * sizeof(PageBuf));   // kThreadsL + 1
+  uint8_t* qlds_all = smem + 2 * sizeof(PageBuf);                  // kMaxWaves x kQLdsWave
+  int* tmp = reinterpret_cast<int*>(qlds_all + kMaxWaves * kQLdsWave);  // kThreadsL + 1
   int* pref = tmp + kThreadsL + 1;                                  // B + 1
   constexpr int NT = 64 * NW;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int h = lane >> 5;        // half-wave
-  const int n = lane & 31;        // head within the wave's 32 / MFMA column
+  const int g = lane >> 4;        // 16-lane group: MFMA k slice / output row quad
+  const int n = lane & 15;        // MFMA row (A) or column (B, output)
 
   // the prefix needs all kThreadsL slots of tmp; threads beyond NT count 0
   const int T = [&] {
@@ -199,38 +210,50 @@ void latent_partial_kernel(LatArgs a) {
   const float c0 = a.sm_scale * kLog2eL;
   const int head0 = wave * kHeadsPerWave;
 
-  int g = lo;
-  while (g < hi) {
-    // sequence owning global page g: last s with pref[s] <= g
+  int gp = lo;
+  while (gp < hi) {
+    // sequence owning global page gp: last s with pref[s] <= gp
     int sl = 0, sh = a.B;
     while (sh - sl > 1) {
       const int mid = (sl + sh) >> 1;
-      if (pref[mid] <= g) sl = mid; else sh = mid;
+      if (pref[mid] <= gp) sl = mid; else sh = mid;
     }
     const int s = __builtin_amdgcn_readfirstlane(sl);
-    const int j0 = g - pref[s];
+    const int j0 = gp - pref[s];
     const int j1 = min(hi, pref[s + 1]) - pref[s];
     const int len = a.lens[s];
     const int32_t* btrow = a.bt + (int64_t)s * a.max_blocks;
-    auto part_of = [&](int sq) {
-      return a.part + ((int64_t)(w + sq) * a.Hq + head0 + n) * kRow;
+    auto part_of = [&](int sq, int ht) {
+      return a.part + ((int64_t)(w + sq) * a.Hq + head0 + 16 * ht + n) * kRow;
     };
 
     // ---- Q of this wave's heads, resident for the fragment --------------
-    // B operand of k-step k: lane (head n, half h) holds dims 16k + 8h .. +7.
-    bf16x8_t qreg[kGroups];
+    // B operand of k-step k, head tile ht: lane (head 16 ht + n, group g)
+    // holds dims 32k + 8g .. +7. Steps below kQReg stay in registers; the
+    // others go to this wave's LDS region as [k - kQReg][ht][lane][16 bytes]
+    // (only this wave reads it, after its own writes).
+    bf16x8_t qreg[2][kQReg];
+    uint8_t* qlds = qlds_all + wave * kQLdsWave + lane * 16;
     {
-      const uint16_t* qrow = a.q + ((int64_t)s * a.Hq + head0 + n) * kDk + 8 * h;
+      const uint16_t* qrow = a.q + ((int64_t)s * a.Hq + head0 + n) * kDk + 8 * g;
 #pragma unroll
-      for (int k = 0; k < kGroups; ++k)
-        qreg[k] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(qrow + 16 * k));
+      for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+        for (int k = 0; k < kKSteps; ++k) {
+          const uint4 v = *reinterpret_cast<const uint4*>(qrow + 16 * ht * kDk + 32 * k);
+          if (k < kQReg)
+            qreg[ht][k] = __builtin_bit_cast(bf16x8_t, v);
+          else
+            *reinterpret_cast<uint4*>(qlds + ((k - kQReg) * 2 + ht) * 1024) = v;
+        }
     }
 
-    f32x16_t acc[kDv / 32];
+    f32x4_t acc[kDTiles][2];
 #pragma unroll
-    for (int d = 0; d < kDv / 32; ++d) acc[d] = f32x16_t{};
-    float m = -INFINITY;   // running max of y for head n (same in both halves)
-    float l = 0.0f;        // this lane's tokens' share of the weight sum
+    for (int c = 0; c < kDTiles; ++c) acc[c][0] = acc[c][1] = f32x4_t{};
+    // running max of y per head tile (the same in the four lanes of a head)
+    float m0 = -INFINITY, m1 = -INFINITY;
+    float l0 = 0.0f, l1 = 0.0f;   // this lane's tokens' share of the weight sums
     bool bad = false;
 
     // ---- page staging ------------------------------------------------------
@@ -239,7 +262,6 @@ void latent_partial_kernel(LatArgs a) {
     // bytes land at the wave-uniform LDS address + 16 * lane), so staging
     // takes no registers. The copy of page j+1 runs while page j computes.
     constexpr int kWaveChunks = kPageBytes / (16 * 64);    // 36 wave copies
-    float sc_next = 0.0f;
     auto fetch = [&](int j, PageBuf& pb) {
       int page = btrow[j];
       if (page < 0 || page >= a.P) {
@@ -275,12 +297,25 @@ void latent_partial_kernel(LatArgs a) {
                      :: "s"(l0 + (uint32_t)i * 1024u), "v"(lane16), "s"(srcu + (int64_t)i * 1024)
                      : "memory");
       }
-      if (tid < kS) sc_next = a.tscale[(int64_t)page * kS + tid];
+      // the page's 64 scales, by wave 0: lane i's 4 bytes land at sraw + 4 i
+      if (wv == 0) {
+        const uint32_t ls = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(uintptr_t)((__attribute__((address_space(3))) float*)pb.sraw));
+        const uint64_t t64 = (uint64_t)(uintptr_t)(a.tscale + (int64_t)page * kS);
+        const uint32_t t_lo = __builtin_amdgcn_readfirstlane((uint32_t)t64);
+        const uint32_t t_hi = __builtin_amdgcn_readfirstlane((uint32_t)(t64 >> 32));
+        const float* tsu = (const float*)(uintptr_t)(((uint64_t)t_hi << 32) | t_lo);
+        uint32_t lane4;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0\n\t"
+                     "v_lshlrev_b32 %0, 2, %0" : "=v"(lane4));
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+                     :: "s"(ls), "v"(lane4), "s"(tsu) : "memory");
+      }
     };
     // After the copy of page j has landed: zero the codes of tokens past the
     // end (they then add nothing, whatever the slot held) and fill the
     // per-token arrays.
-    auto finish = [&](int j, PageBuf& pb, float sc) {
+    auto finish = [&](int j, PageBuf& pb) {
       const int valid = min(kS, len - j * kS);   // tokens of this page in use
       if (valid < kS) {
         for (int c = tid; c < kPageBytes / 16; c += NT)
@@ -288,6 +323,7 @@ void latent_partial_kernel(LatArgs a) {
       }
       if (tid < kS) {
         // v_log_f32 is log2
+        const float sc = pb.sraw[tid];
         const bool live = tid < valid;
         pb.a[tid] = live ? sc * c0 : 0.0f;
         pb.b[tid] = live ? __builtin_amdgcn_logf(sc) : -INFINITY;
@@ -301,168 +337,209 @@ void latent_partial_kernel(LatArgs a) {
       // page j's copy (and every earlier load) complete, then publish
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      // The next page's copy goes out first: the other buffer's last readers
-      // (page j - 1) passed the barrier above. Page j's scales came with its
-      // copy; keep them before the next copy's scale load replaces them.
-      const float sc_cur = sc_next;
+      // Page j's per-token arrays first, then the next page's copy (the other
+      // buffer's last readers, page j - 1, passed the barrier above). Nothing
+      // after the copy waits on the vector memory counter until the top of
+      // the next page: a wait there (a register reload, a scale load) would
+      // wait for the whole copy and serialise it with this page's products.
+      finish(j, pb);
       if (j + 1 < j1) fetch(j + 1, buf[(j + 1 - j0) & 1]);
-      finish(j, pb, sc_cur);
       __syncthreads();
 
-      // ---- QK: S^T (64 tokens x 32 heads) as two 32x32 tiles --------------
-      // A operand of k-step k, tile t: lane (token 32t + n, half h) holds the
-      // codes of dims 16k + 8h .. +7 (8 bytes, one LDS read). Reads run two
-      // steps ahead; the scheduling barrier per step keeps the compiler from
-      // hoisting every read and conversion (a register each).
-      f32x16_t st[2] = {f32x16_t{}, f32x16_t{}};
+      // ---- QK: S^T (64 tokens x 32 heads) as 4 x 2 tiles of 16 x 16 --------
+      // A operand of k-step k, token tile t: lane (row i = n, group g) holds
+      // the codes of dims 32k + 8g .. +7 of the tile's row-i token (column
+      // group 2k + g/2, bytes 8(g&1) .. +7 of its 16-byte slot; one 8-byte LDS
+      // read). Unit u = 4k + t; reads run four units ahead, and the
+      // scheduling barrier per unit keeps the compiler from hoisting every
+      // read and conversion (a register each).
+      f32x4_t st[4][2];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) st[t][0] = st[t][1] = f32x4_t{};
       {
-        // reads run two steps ahead: a step converts its codes, then reuses
-        // their registers for the read two steps on, then issues its MFMAs
-        const uint8_t* rowp = pb.codes + n * 16 + 8 * h;
-        auto rdk = [&](int k, int t) -> uint2 {
-          return *reinterpret_cast<const uint2*>(rowp + k * (kS * 16) + t * (32 * 16));
+        const uint8_t* rowe = pb.codes + (g >> 1) * (kS * 16) + n * 16 + 8 * (g & 1);
+        const uint8_t* rowo = pb.codes + (g >> 1) * (kS * 16) + (n ^ 8) * 16 + 8 * (g & 1);
+        auto rdk = [&](int u) -> uint2 {
+          const int k = u >> 2, t = u & 3;
+          return *reinterpret_cast<const uint2*>((t & 1 ? rowo : rowe) + k * (2 * kS * 16) +
+                                                 t * (16 * 16));
         };
-        uint2 ra[2] = {rdk(0, 0), rdk(1, 0)};
-        uint2 rb[2] = {rdk(0, 1), rdk(1, 1)};
-        sfor<0, kGroups>::run([&](auto K) {
-          constexpr int k = decltype(K)::value;
-          const uint2 c0 = ra[k & 1], c1 = rb[k & 1];
-          const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0.x, 1.0f, false);
-          const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0.x, 1.0f, true);
-          const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0.y, 1.0f, false);
-          const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0.y, 1.0f, true);
-          const bf16x2_t u0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1.x, 1.0f, false);
-          const bf16x2_t u1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1.x, 1.0f, true);
-          const bf16x2_t u2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1.y, 1.0f, false);
-          const bf16x2_t u3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1.y, 1.0f, true);
-          if constexpr (k + 2 < kGroups) {
-            ra[k & 1] = rdk(k + 2, 0);
-            rb[k & 1] = rdk(k + 2, 1);
+        constexpr int kAhead = 4;
+        constexpr int kUnits = 4 * kKSteps;
+        uint2 ring[kAhead];
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u) ring[u] = rdk(u);
+        // LDS-resident Q of step k is read during step k - 1 (unit t = 1)
+        auto rdq = [&](int k, int ht) -> bf16x8_t {
+          return __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const uint4*>(qlds + ((k - kQReg) * 2 + ht) * 1024));
+        };
+        bf16x8_t qn[2][2];
+        sfor<0, kUnits>::run([&](auto U) {
+          constexpr int u = decltype(U)::value;
+          constexpr int k = u >> 2, t = u & 3;
+          const uint2 cw = ring[u % kAhead];
+          const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw.x, 1.0f, false);
+          const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw.x, 1.0f, true);
+          const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw.y, 1.0f, false);
+          const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw.y, 1.0f, true);
+          if constexpr (u + kAhead < kUnits) ring[u % kAhead] = rdk(u + kAhead);
+          if constexpr (t == 1 && k + 1 >= kQReg && k + 1 < kKSteps) {
+            qn[(k + 1) & 1][0] = rdq(k + 1, 0);
+            qn[(k + 1) & 1][1] = rdq(k + 1, 1);
           }
-          const bf16x8_t a0 = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-          const bf16x8_t a1 = {u0.x, u0.y, u1.x, u1.y, u2.x, u2.y, u3.x, u3.y};
-          st[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[k], st[0], 0, 0, 0);
-          st[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[k], st[1], 0, 0, 0);
+          const bf16x8_t av = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+          if constexpr (k < kQReg) {
+            st[t][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[0][k], st[t][0], 0, 0, 0);
+            st[t][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[1][k], st[t][1], 0, 0, 0);
+          } else {
+            st[t][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qn[k & 1][0], st[t][0], 0, 0, 0);
+            st[t][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qn[k & 1][1], st[t][1], 0, 0, 0);
+          }
           __builtin_amdgcn_sched_barrier(0);
         });
       }
 
       // ---- softmax (log2 units, scale folded in) --------------------------
-      // register r of tile t holds token 32t + (r/4)*8 + 4h + r%4
-      float bm = -INFINITY;
+      // st[t][ht] register r holds token 16t + 4(g ^ 2(t&1)) + r of head
+      // 16 ht + n (row 4g + r of the tile)
+      float bm0 = -INFINITY, bm1 = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 4; ++t) {
+        const int t0 = 16 * t + 4 * (g ^ (2 * (t & 1)));
+        const float4 av = *reinterpret_cast<const float4*>(pb.a + t0);
+        const float4 bv = *reinterpret_cast<const float4*>(pb.b + t0);
+        const float aa[4] = {av.x, av.y, av.z, av.w};
+        const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int t0 = 32 * t + r4 * 8 + 4 * h;
-          const float4 av = *reinterpret_cast<const float4*>(pb.a + t0);
-          const float4 bv = *reinterpret_cast<const float4*>(pb.b + t0);
-          const float aa[4] = {av.x, av.y, av.z, av.w};
-          const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float v = fmaf(st[t][4 * r4 + i], aa[i], bb[i]);
-            st[t][4 * r4 + i] = v;
-            bm = fmaxf(bm, v);
-          }
+        for (int r = 0; r < 4; ++r) {
+          const float v0 = fmaf(st[t][0][r], aa[r], bb[r]);
+          const float v1 = fmaf(st[t][1][r], aa[r], bb[r]);
+          st[t][0][r] = v0;
+          st[t][1][r] = v1;
+          bm0 = fmaxf(bm0, v0);
+          bm1 = fmaxf(bm1, v1);
         }
       }
-      bm = fmaxf(bm, shfl_xor_f32(bm, 32));
-      if (__ballot(bm > m + kTauL) != 0) {
-        // some head's max moved by more than the threshold: rescale those
-        const bool mv = bm > m + kTauL;
-        const float mn = mv ? bm : m;
-        if (m != -INFINITY) {   // uniform: every head has a finite max after page 1
-          const float alpha = mv ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;
-          l *= alpha;
-          // acc *= alpha, as a round trip through this fragment's partial
-          // slot (written again at the end): multiplying the accumulators in
-          // place would pull all of them out of the matrix-core registers
-          rescale_via(part_of(s), acc, alpha);
-        }
-        m = mn;
-      }
-      // p' = 2^(y - m), packed to f16 as the B operand of PV: k-step
-      // ks = 2t + s2 takes registers 8*s2 .. 8*s2+7 of tile t
-      f16x8_t pk[4];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int t0 = 32 * t + r4 * 8 + 4 * h;
-          const float4 iv = *reinterpret_cast<const float4*>(pb.inv + t0);
-          const float ii[4] = {iv.x, iv.y, iv.z, iv.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = __builtin_amdgcn_exp2f(st[t][4 * r4 + i] - m);
-            l = fmaf(p, ii[i], l);
-            pk[2 * t + r4 / 2][4 * (r4 & 1) + i] = (_Float16)p;
+      bm0 = fmaxf(bm0, shfl_xor_f32(bm0, 16));
+      bm1 = fmaxf(bm1, shfl_xor_f32(bm1, 16));
+      bm0 = fmaxf(bm0, shfl_xor_f32(bm0, 32));
+      bm1 = fmaxf(bm1, shfl_xor_f32(bm1, 32));
+      {
+        const bool mv0 = bm0 > m0 + kTauL;
+        const bool mv1 = bm1 > m1 + kTauL;
+        if (__ballot(mv0 || mv1) != 0) {
+          // some head's max moved by more than the threshold: rescale those
+          const float mn0 = mv0 ? bm0 : m0;
+          const float mn1 = mv1 ? bm1 : m1;
+          if (m0 != -INFINITY) {   // uniform: every head has a finite max after page 1
+            const float al0 = mv0 ? __builtin_amdgcn_exp2f(m0 - mn0) : 1.0f;
+            const float al1 = mv1 ? __builtin_amdgcn_exp2f(m1 - mn1) : 1.0f;
+            l0 *= al0;
+            l1 *= al1;
+            // acc *= alpha, as a round trip through this fragment's partial
+            // slot (written again at the end): multiplying the accumulators
+            // in place would pull all of them out of the matrix-core registers
+            rescale_via(part_of(s, 0), part_of(s, 1), acc, al0, al1);
           }
+          m0 = mn0;
+          m1 = mn1;
+        }
+      }
+      // p' = 2^(y - m), packed to f16 as the B operand of PV: k-step kk, head
+      // tile ht takes registers 0..3 of token tiles 2kk and 2kk+1
+      f16x8_t pk[2][2];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int t0 = 16 * t + 4 * (g ^ (2 * (t & 1)));
+        const float4 iv = *reinterpret_cast<const float4*>(pb.inv + t0);
+        const float ii[4] = {iv.x, iv.y, iv.z, iv.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p0 = __builtin_amdgcn_exp2f(st[t][0][r] - m0);
+          const float p1 = __builtin_amdgcn_exp2f(st[t][1][r] - m1);
+          l0 = fmaf(p0, ii[r], l0);
+          l1 = fmaf(p1, ii[r], l1);
+          pk[t >> 1][0][4 * (t & 1) + r] = (_Float16)p0;
+          pk[t >> 1][1][4 * (t & 1) + r] = (_Float16)p1;
         }
       }
 
       // ---- PV: O^T (512 dims x 32 heads) += V^T P^T ------------------------
-      // k-step ks = 2t + s2: row b of the transpose read is token
-      // 16ks + (b/4)*8 + 4hh + b%4 where hh is the half-wave of the receiving
-      // lanes (lanes 0-31 receive k = 0..7, lanes 32-63 k = 8..15). In 16-lane
-      // group gq (hh = gq/2, dims 16*(gq%2) + 0..15 of the tile), lane 2b + e
-      // supplies token row b, bytes 8e..8e+7 of its 16 dims.
+      // k-step kk, 16-lane group g: row b of the transpose read is the token
+      // whose p sits in element b of the group's B operand: 32kk + 4g + b
+      // (b < 4, tile 2kk) or 32kk + 16 + 4(g ^ 2) + b - 4 (b >= 4, tile
+      // 2kk+1). Lane 2b + e supplies that token's bytes 8e .. 8e+7 of
+      // column group c (dims 16c .. 16c+15); lane i receives dim 16c + i.
       {
-        const int gq = lane >> 4;
-        const int hh = gq >> 1;
         const int li = lane & 15;
         const int bb = li >> 1;
         const int e = li & 1;
-        const uint8_t* vbase = pb.codes + ((bb >> 2) * 8 + 4 * hh + (bb & 3)) * 16 + 8 * e +
-                               (gq & 1) * (kS * 16);
-        auto rd = [&](int ks, int d) -> i32x2_t {
+        const int tok = bb < 4 ? 4 * g + bb : 16 + 4 * (g ^ 2) + (bb - 4);
+        const uint8_t* vbase = pb.codes + tok * 16 + 8 * e;
+        auto rd = [&](int u) -> i32x2_t {   // unit u = 32 kk + c
+          const int kk = u / kDTiles, c = u % kDTiles;
           return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (__attribute__((address_space(3))) i32x2_t*)(vbase + 16 * ks * 16 +
-                                                           2 * d * (kS * 16)));
+              (__attribute__((address_space(3))) i32x2_t*)(vbase + kk * (32 * 16) +
+                                                           c * (kS * 16)));
         };
-        // reads run two steps ahead (step I = ks * 16 + d), as in QK
-        constexpr int kPV = 4 * (kDv / 32);
-        i32x2_t rr[2] = {rd(0, 0), rd(0, 1)};
+        constexpr int kPV = 2 * kDTiles;
+        i32x2_t rr[2] = {rd(0), rd(1)};
         sfor<0, kPV>::run([&](auto I) {
           constexpr int i = decltype(I)::value;
-          constexpr int ks = i / (kDv / 32);
-          constexpr int d = i % (kDv / 32);
+          constexpr int kk = i / kDTiles;
+          constexpr int c = i % kDTiles;
           const i32x2_t cw = rr[i & 1];
           const f16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)cw.x, 1.0f, false);
           const f16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)cw.x, 1.0f, true);
           const f16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)cw.y, 1.0f, false);
           const f16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)cw.y, 1.0f, true);
-          if constexpr (i + 2 < kPV) rr[i & 1] = rd((i + 2) / (kDv / 32), (i + 2) % (kDv / 32));
+          if constexpr (i + 2 < kPV) rr[i & 1] = rd(i + 2);
           const f16x8_t av = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y, v3.x, v3.y};
-          acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pk[ks], acc[d], 0, 0, 0);
+          // inline asm pins the accumulators to AGPRs, leaving the VGPRs to
+          // the score tiles; s_nop 1 covers a VALU write of av, pk or acc
+          // just before (two wait states)
+          asm volatile("s_nop 1\n\t"
+                       "v_mfma_f32_16x16x32_f16 %0, %2, %3, %0\n\t"
+                       "v_mfma_f32_16x16x32_f16 %1, %2, %4, %1"
+                       : "+a"(acc[c][0]), "+a"(acc[c][1])
+                       : "v"(av), "v"(pk[kk][0]), "v"(pk[kk][1]));
           __builtin_amdgcn_sched_barrier(0);
         });
       }
     }
 
+    // the last PV results land before the accumulators are read (24 wait
+    // states; the compiler does not see the matrix-core writes in the asm)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     // ---- partial of this fragment -------------------------------------------
-    float* part = part_of(s);
-    const float lt = l + shfl_xor_f32(l, 32);
+    float* part0 = part_of(s, 0);
+    float* part1 = part_of(s, 1);
+    l0 += shfl_xor_f32(l0, 16);
+    l1 += shfl_xor_f32(l1, 16);
+    l0 += shfl_xor_f32(l0, 32);
+    l1 += shfl_xor_f32(l1, 32);
     const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
     if (any_bad) {
-      if (h == 0) part[kDv] = __builtin_nanf("");
-    } else {
-      // acc[d] register r: dim 32d + (r/4)*8 + 4h + r%4 of head n
-#pragma unroll
-      for (int d = 0; d < kDv / 32; ++d) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          float4 v = make_float4(acc[d][4 * r4], acc[d][4 * r4 + 1], acc[d][4 * r4 + 2],
-                                 acc[d][4 * r4 + 3]);
-          *reinterpret_cast<float4*>(part + 32 * d + r4 * 8 + 4 * h) = v;
-        }
+      if (g == 0) {
+        part0[kDv] = __builtin_nanf("");
+        part1[kDv] = __builtin_nanf("");
       }
-      if (h == 0) {
-        part[kDv] = m;
-        part[kDv + 1] = lt;
+    } else {
+      // acc[c][ht] register r: dim 16c + 4g + r of head 16 ht + n
+#pragma unroll
+      for (int c = 0; c < kDTiles; ++c) {
+        *reinterpret_cast<f32x4_t*>(part0 + 16 * c + 4 * g) = acc[c][0];
+        *reinterpret_cast<f32x4_t*>(part1 + 16 * c + 4 * g) = acc[c][1];
+      }
+      if (g == 0) {
+        part0[kDv] = m0;
+        part0[kDv + 1] = l0;
+        part1[kDv] = m1;
+        part1[kDv + 1] = l1;
       }
     }
-    g = pref[s] + j1;
+    gp = pref[s] + j1;
     __syncthreads();
   }
 }
@@ -532,7 +609,8 @@ size_t lat_slot_bytes(const pda_attn_shape& sh) {
 }
 
 size_t lat_lds_bytes(int B) {
-  return 2 * sizeof(PageBuf) + (size_t)(kThreadsL + 1 + B + 1) * sizeof(int);
+  return 2 * sizeof(PageBuf) + (size_t)kMaxWaves * kQLdsWave +
+         (size_t)(kThreadsL + 1 + B + 1) * sizeof(int);
 }
 
 typedef void (*lat_kernel_t)(LatArgs);
