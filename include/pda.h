@@ -231,7 +231,7 @@ size_t paged_decode_attn_workspace_bytes(const pda_attn_shape* shape,
  *  Supported: FP8 or BF16, PER_HEAD/NONE, Dk == Dv == 128, Hq/Hkv in
  *  {1,2,4,8}, S in {16, 32, 64}, num_seqs <= 16384 (vector-ALU kernel);
  *  and latent FP8 PER_TOKEN, Hkv == 1, Dk == 576, Dv == 512, v_in_k,
- *  S == 64, Hq in {32, 64, 96, 128}, num_seqs <= 8192 (matrix-core kernel;
+ *  S == 64, Hq in {32, 64, 96, 128}, num_seqs <= 2048 (matrix-core kernel;
  *  split_tokens is ignored there: the valid pages of all sequences are cut
  *  into one equal range per compute unit, and the workspace holds one
  *  partial per (range, sequence) pair that meets).
