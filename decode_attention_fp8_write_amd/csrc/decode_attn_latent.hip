@@ -25,7 +25,10 @@
 //    the current one is computed). Tokens past the end are written as zero codes
 //    with weight 0, so they contribute nothing and poisoned bytes are never
 //    read into the arithmetic.
-//  * wave w owns query heads [32w, 32w+32), as two tiles of 16. Every
+//  * wave w owns query heads [16w, 16w+16), one 16-head tile, so 128 heads
+//    take eight waves, two per SIMD: one wave's conversions and softmax
+//    overlap the other's matrix products (a wave's own instruction stream
+//    is in order). Every
 //    product runs on 16x16x32 matrix-core tiles, whose operand reads from
 //    the token-major page hit every LDS bank once per half-wave (a lane reads
 //    8 bytes; the 32 lanes of a half-wave cover 16 tokens' full 16-byte
@@ -62,11 +65,8 @@ constexpr int kS = 64;              // page size
 constexpr int kKSteps = kDk / 32;   // 32-dim QK k-steps per token
 constexpr int kDTiles = kDv / 16;   // 16-dim PV output tiles
 constexpr int kPageBytes = kDk * kS;
-constexpr int kHeadsPerWave = 32;
-constexpr int kMaxWaves = 4;
-constexpr int kThreadsL = 64 * kMaxWaves;
-static_assert((kDk * kS) / (16 * 64) % 4 == 0 && (kDk * kS) / (16 * 64) % 3 == 0,
-              "page copies must split evenly over 1..4 waves");
+constexpr int kMaxWavesL = 8;
+constexpr int kMaxThreadsL = 64 * kMaxWavesL;
 constexpr float kTauL = 8.0f;
 constexpr float kLog2eL = 1.4426950408889634f;
 constexpr int kHdrL = 64;           // header ints, then pref[B+1]
@@ -76,7 +76,8 @@ constexpr int kMaxSeqsL = 2048;
 // (registers would spill otherwise; a spill reload waits on the memory
 // counter that also tracks the page copy in flight)
 constexpr int kQReg = 9;
-constexpr int kQLdsWave = (kKSteps - kQReg) * 2 * 64 * 16;   // bytes per wave
+constexpr int kQLdsTile = (kKSteps - kQReg) * 64 * 16;   // bytes per 16-head tile
+constexpr int kMaxTilesL = 8;                             // 128 heads
 
 template <int F, int L>
 struct sfor {
@@ -131,34 +132,50 @@ struct PageBuf {
 };
 
 // acc *= alpha for the (rare) running-max move, through global memory:
-// store the accumulators (the lane's two head rows, layout of the partial),
-// wait, and load them back scaled. The rows belong to this lane alone.
-// acc[c][ht] register r: dim 16c + 4g + r of head 16 ht + n.
-__device__ __forceinline__ void rescale_via(float* row0, float* row1, f32x4_t (&acc)[kDTiles][2],
-                                            float alpha0, float alpha1) {
+// store the accumulators (the lane's head rows, layout of the partial),
+// wait, and load them back scaled, one tile at a time (the scheduling
+// barriers keep the compiler from hoisting every load, whose registers
+// would push values out to scratch). The register reloads the compiler
+// still leaves pending at the end of this branch make the first PV product
+// of every page wait for the page copy in flight; measured, that costs less
+// than issuing the copy after this point.
+// acc[c][ht] register r: dim 16c + 4g + r of head tile ht, column n.
+constexpr int kRescaleTiles = 1;
+template <int HT>
+__device__ __forceinline__ void rescale_via(float* const (&row)[HT], f32x4_t (&acc)[kDTiles][HT],
+                                            const float (&alpha)[HT]) {
   const int g = __lane_id() >> 4;
 #pragma unroll
-  for (int c = 0; c < kDTiles; ++c) {
-    *reinterpret_cast<f32x4_t*>(row0 + 16 * c + 4 * g) = acc[c][0];
-    *reinterpret_cast<f32x4_t*>(row1 + 16 * c + 4 * g) = acc[c][1];
-  }
+  for (int c = 0; c < kDTiles; ++c)
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+      *reinterpret_cast<f32x4_t*>(row[ht] + 16 * c + 4 * g) = acc[c][ht];
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  sfor<0, kDTiles / kRescaleTiles>::run([&](auto C4) {
+    constexpr int c0 = kRescaleTiles * decltype(C4)::value;
 #pragma unroll
-  for (int c = 0; c < kDTiles; ++c) {
-    acc[c][0] = *reinterpret_cast<const f32x4_t*>(row0 + 16 * c + 4 * g) * alpha0;
-    acc[c][1] = *reinterpret_cast<const f32x4_t*>(row1 + 16 * c + 4 * g) * alpha1;
-  }
+    for (int c = c0; c < c0 + kRescaleTiles; ++c)
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+        acc[c][ht] = *reinterpret_cast<const f32x4_t*>(row[ht] + 16 * c + 4 * g) * alpha[ht];
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_sched_barrier(0);
+  });
 }
 
-template <int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// NW waves of HT 16-head tiles each (NW * HT * 16 query heads). With one
+// tile per wave the eight waves of 128 heads run two to a SIMD, so one
+// wave's softmax and conversions overlap the other's matrix products.
+template <int NW, int HT>
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(HT == 1 ? 2 : 1, HT == 1 ? 2 : 1)))
 void latent_partial_kernel(LatArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   PageBuf* buf = reinterpret_cast<PageBuf*>(smem);                 // [2]
-  uint8_t* qlds_all = smem + 2 * sizeof(PageBuf);                  // kMaxWaves x kQLdsWave
-  int* tmp = reinterpret_cast<int*>(qlds_all + kMaxWaves * kQLdsWave);  // kThreadsL + 1
-  int* pref = tmp + kThreadsL + 1;                                  // B + 1
+  uint8_t* qlds_all = smem + 2 * sizeof(PageBuf);                  // kMaxTilesL x kQLdsTile
+  int* tmp = reinterpret_cast<int*>(qlds_all + kMaxTilesL * kQLdsTile);  // kMaxThreadsL + 1
+  int* pref = tmp + kMaxThreadsL + 1;                               // B + 1
   constexpr int NT = 64 * NW;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -166,7 +183,6 @@ void latent_partial_kernel(LatArgs a) {
   const int g = lane >> 4;        // 16-lane group: MFMA k slice / output row quad
   const int n = lane & 15;        // MFMA row (A) or column (B, output)
 
-  // the prefix needs all kThreadsL slots of tmp; threads beyond NT count 0
   const int T = [&] {
     const int per = (a.B + NT - 1) / NT;
     const int beg = min(a.B, tid * per);
@@ -208,7 +224,7 @@ void latent_partial_kernel(LatArgs a) {
   const int lo = (int)((long long)w * T / W);
   const int hi = (int)((long long)(w + 1) * T / W);
   const float c0 = a.sm_scale * kLog2eL;
-  const int head0 = wave * kHeadsPerWave;
+  const int head0 = wave * 16 * HT;
 
   int gp = lo;
   while (gp < hi) {
@@ -223,37 +239,44 @@ void latent_partial_kernel(LatArgs a) {
     const int j1 = min(hi, pref[s + 1]) - pref[s];
     const int len = a.lens[s];
     const int32_t* btrow = a.bt + (int64_t)s * a.max_blocks;
-    auto part_of = [&](int sq, int ht) {
-      return a.part + ((int64_t)(w + sq) * a.Hq + head0 + 16 * ht + n) * kRow;
-    };
+    float* prow[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+      prow[ht] = a.part + ((int64_t)(w + s) * a.Hq + head0 + 16 * ht + n) * kRow;
 
     // ---- Q of this wave's heads, resident for the fragment --------------
     // B operand of k-step k, head tile ht: lane (head 16 ht + n, group g)
     // holds dims 32k + 8g .. +7. Steps below kQReg stay in registers; the
     // others go to this wave's LDS region as [k - kQReg][ht][lane][16 bytes]
     // (only this wave reads it, after its own writes).
-    bf16x8_t qreg[2][kQReg];
-    uint8_t* qlds = qlds_all + wave * kQLdsWave + lane * 16;
+    bf16x8_t qreg[HT][kQReg];
+    uint8_t* qlds = qlds_all + wave * HT * kQLdsTile + lane * 16;
     {
       const uint16_t* qrow = a.q + ((int64_t)s * a.Hq + head0 + n) * kDk + 8 * g;
 #pragma unroll
-      for (int ht = 0; ht < 2; ++ht)
+      for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
         for (int k = 0; k < kKSteps; ++k) {
           const uint4 v = *reinterpret_cast<const uint4*>(qrow + 16 * ht * kDk + 32 * k);
           if (k < kQReg)
             qreg[ht][k] = __builtin_bit_cast(bf16x8_t, v);
           else
-            *reinterpret_cast<uint4*>(qlds + ((k - kQReg) * 2 + ht) * 1024) = v;
+            *reinterpret_cast<uint4*>(qlds + ((k - kQReg) * HT + ht) * 1024) = v;
         }
     }
 
-    f32x4_t acc[kDTiles][2];
+    f32x4_t acc[kDTiles][HT];
 #pragma unroll
-    for (int c = 0; c < kDTiles; ++c) acc[c][0] = acc[c][1] = f32x4_t{};
+    for (int c = 0; c < kDTiles; ++c)
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) acc[c][ht] = f32x4_t{};
     // running max of y per head tile (the same in the four lanes of a head)
-    float m0 = -INFINITY, m1 = -INFINITY;
-    float l0 = 0.0f, l1 = 0.0f;   // this lane's tokens' share of the weight sums
+    float m[HT], l[HT];   // l: this lane's tokens' share of the weight sum
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      m[ht] = -INFINITY;
+      l[ht] = 0.0f;
+    }
     bool bad = false;
 
     // ---- page staging ------------------------------------------------------
@@ -291,8 +314,9 @@ void latent_partial_kernel(LatArgs a) {
       asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0\n\t"
                    "v_lshlrev_b32 %0, 4, %0" : "=v"(lane16));
 #pragma unroll
-      for (int ii = 0; ii < kWaveChunks / NW; ++ii) {
+      for (int ii = 0; ii < (kWaveChunks + NW - 1) / NW; ++ii) {
         const int i = ii * NW + wv;
+        if (kWaveChunks % NW != 0 && i >= kWaveChunks) break;   // uniform
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                      :: "s"(l0 + (uint32_t)i * 1024u), "v"(lane16), "s"(srcu + (int64_t)i * 1024)
                      : "memory");
@@ -346,16 +370,18 @@ void latent_partial_kernel(LatArgs a) {
       if (j + 1 < j1) fetch(j + 1, buf[(j + 1 - j0) & 1]);
       __syncthreads();
 
-      // ---- QK: S^T (64 tokens x 32 heads) as 4 x 2 tiles of 16 x 16 --------
+      // ---- QK: S^T (64 tokens x 16 HT heads) as 4 x HT tiles of 16 x 16 --
       // A operand of k-step k, token tile t: lane (row i = n, group g) holds
       // the codes of dims 32k + 8g .. +7 of the tile's row-i token (column
       // group 2k + g/2, bytes 8(g&1) .. +7 of its 16-byte slot; one 8-byte LDS
       // read). Unit u = 4k + t; reads run four units ahead, and the
       // scheduling barrier per unit keeps the compiler from hoisting every
       // read and conversion (a register each).
-      f32x4_t st[4][2];
+      f32x4_t st[4][HT];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) st[t][0] = st[t][1] = f32x4_t{};
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) st[t][ht] = f32x4_t{};
       {
         const uint8_t* rowe = pb.codes + (g >> 1) * (kS * 16) + n * 16 + 8 * (g & 1);
         const uint8_t* rowo = pb.codes + (g >> 1) * (kS * 16) + (n ^ 8) * 16 + 8 * (g & 1);
@@ -372,9 +398,9 @@ void latent_partial_kernel(LatArgs a) {
         // LDS-resident Q of step k is read during step k - 1 (unit t = 1)
         auto rdq = [&](int k, int ht) -> bf16x8_t {
           return __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const uint4*>(qlds + ((k - kQReg) * 2 + ht) * 1024));
+              bf16x8_t, *reinterpret_cast<const uint4*>(qlds + ((k - kQReg) * HT + ht) * 1024));
         };
-        bf16x8_t qn[2][2];
+        bf16x8_t qn[2][HT];
         sfor<0, kUnits>::run([&](auto U) {
           constexpr int u = decltype(U)::value;
           constexpr int k = u >> 2, t = u & 3;
@@ -385,16 +411,16 @@ void latent_partial_kernel(LatArgs a) {
           const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw.y, 1.0f, true);
           if constexpr (u + kAhead < kUnits) ring[u % kAhead] = rdk(u + kAhead);
           if constexpr (t == 1 && k + 1 >= kQReg && k + 1 < kKSteps) {
-            qn[(k + 1) & 1][0] = rdq(k + 1, 0);
-            qn[(k + 1) & 1][1] = rdq(k + 1, 1);
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) qn[(k + 1) & 1][ht] = rdq(k + 1, ht);
           }
           const bf16x8_t av = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-          if constexpr (k < kQReg) {
-            st[t][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[0][k], st[t][0], 0, 0, 0);
-            st[t][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[1][k], st[t][1], 0, 0, 0);
-          } else {
-            st[t][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qn[k & 1][0], st[t][0], 0, 0, 0);
-            st[t][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qn[k & 1][1], st[t][1], 0, 0, 0);
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) {
+            if constexpr (k < kQReg)
+              st[t][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[ht][k], st[t][ht], 0, 0, 0);
+            else
+              st[t][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qn[k & 1][ht], st[t][ht], 0, 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
         });
@@ -403,7 +429,9 @@ void latent_partial_kernel(LatArgs a) {
       // ---- softmax (log2 units, scale folded in) --------------------------
       // st[t][ht] register r holds token 16t + 4(g ^ 2(t&1)) + r of head
       // 16 ht + n (row 4g + r of the tile)
-      float bm0 = -INFINITY, bm1 = -INFINITY;
+      float bm[HT];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) bm[ht] = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int t0 = 16 * t + 4 * (g ^ (2 * (t & 1)));
@@ -412,60 +440,61 @@ void latent_partial_kernel(LatArgs a) {
         const float aa[4] = {av.x, av.y, av.z, av.w};
         const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v0 = fmaf(st[t][0][r], aa[r], bb[r]);
-          const float v1 = fmaf(st[t][1][r], aa[r], bb[r]);
-          st[t][0][r] = v0;
-          st[t][1][r] = v1;
-          bm0 = fmaxf(bm0, v0);
-          bm1 = fmaxf(bm1, v1);
-        }
-      }
-      bm0 = fmaxf(bm0, shfl_xor_f32(bm0, 16));
-      bm1 = fmaxf(bm1, shfl_xor_f32(bm1, 16));
-      bm0 = fmaxf(bm0, shfl_xor_f32(bm0, 32));
-      bm1 = fmaxf(bm1, shfl_xor_f32(bm1, 32));
-      {
-        const bool mv0 = bm0 > m0 + kTauL;
-        const bool mv1 = bm1 > m1 + kTauL;
-        if (__ballot(mv0 || mv1) != 0) {
-          // some head's max moved by more than the threshold: rescale those
-          const float mn0 = mv0 ? bm0 : m0;
-          const float mn1 = mv1 ? bm1 : m1;
-          if (m0 != -INFINITY) {   // uniform: every head has a finite max after page 1
-            const float al0 = mv0 ? __builtin_amdgcn_exp2f(m0 - mn0) : 1.0f;
-            const float al1 = mv1 ? __builtin_amdgcn_exp2f(m1 - mn1) : 1.0f;
-            l0 *= al0;
-            l1 *= al1;
-            // acc *= alpha, as a round trip through this fragment's partial
-            // slot (written again at the end): multiplying the accumulators
-            // in place would pull all of them out of the matrix-core registers
-            rescale_via(part_of(s, 0), part_of(s, 1), acc, al0, al1);
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) {
+            const float v = fmaf(st[t][ht][r], aa[r], bb[r]);
+            st[t][ht][r] = v;
+            bm[ht] = fmaxf(bm[ht], v);
           }
-          m0 = mn0;
-          m1 = mn1;
+      }
+      bool mv[HT];
+      bool any_mv = false;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        bm[ht] = fmaxf(bm[ht], shfl_xor_f32(bm[ht], 16));
+        bm[ht] = fmaxf(bm[ht], shfl_xor_f32(bm[ht], 32));
+        mv[ht] = bm[ht] > m[ht] + kTauL;
+        any_mv |= mv[ht];
+      }
+      if (__ballot(any_mv) != 0) {
+        // some head's max moved by more than the threshold: rescale those
+        float mn[HT], al[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+          mn[ht] = mv[ht] ? bm[ht] : m[ht];
+          al[ht] = mv[ht] ? __builtin_amdgcn_exp2f(m[ht] - mn[ht]) : 1.0f;
         }
+        if (m[0] != -INFINITY) {   // uniform: every head has a finite max after page 1
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) l[ht] *= al[ht];
+          // acc *= alpha, as a round trip through this fragment's partial
+          // slot (written again at the end): multiplying the accumulators in
+          // place would pull all of them out of the matrix-core registers
+          rescale_via<HT>(prow, acc, al);
+        }
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) m[ht] = mn[ht];
       }
       // p' = 2^(y - m), packed to f16 as the B operand of PV: k-step kk, head
       // tile ht takes registers 0..3 of token tiles 2kk and 2kk+1
-      f16x8_t pk[2][2];
+      f16x8_t pk[2][HT];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int t0 = 16 * t + 4 * (g ^ (2 * (t & 1)));
         const float4 iv = *reinterpret_cast<const float4*>(pb.inv + t0);
         const float ii[4] = {iv.x, iv.y, iv.z, iv.w};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p0 = __builtin_amdgcn_exp2f(st[t][0][r] - m0);
-          const float p1 = __builtin_amdgcn_exp2f(st[t][1][r] - m1);
-          l0 = fmaf(p0, ii[r], l0);
-          l1 = fmaf(p1, ii[r], l1);
-          pk[t >> 1][0][4 * (t & 1) + r] = (_Float16)p0;
-          pk[t >> 1][1][4 * (t & 1) + r] = (_Float16)p1;
-        }
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) {
+            const float p = __builtin_amdgcn_exp2f(st[t][ht][r] - m[ht]);
+            l[ht] = fmaf(p, ii[r], l[ht]);
+            pk[t >> 1][ht][4 * (t & 1) + r] = (_Float16)p;
+          }
       }
 
-      // ---- PV: O^T (512 dims x 32 heads) += V^T P^T ------------------------
+      // ---- PV: O^T (512 dims x 16 HT heads) += V^T P^T ---------------------
       // k-step kk, 16-lane group g: row b of the transpose read is the token
       // whose p sits in element b of the group's B operand: 32kk + 4g + b
       // (b < 4, tile 2kk) or 32kk + 16 + 4(g ^ 2) + b - 4 (b >= 4, tile
@@ -499,11 +528,17 @@ void latent_partial_kernel(LatArgs a) {
           // inline asm pins the accumulators to AGPRs, leaving the VGPRs to
           // the score tiles; s_nop 1 covers a VALU write of av, pk or acc
           // just before (two wait states)
-          asm volatile("s_nop 1\n\t"
-                       "v_mfma_f32_16x16x32_f16 %0, %2, %3, %0\n\t"
-                       "v_mfma_f32_16x16x32_f16 %1, %2, %4, %1"
-                       : "+a"(acc[c][0]), "+a"(acc[c][1])
-                       : "v"(av), "v"(pk[kk][0]), "v"(pk[kk][1]));
+          if constexpr (HT == 2)
+            asm volatile("s_nop 1\n\t"
+                         "v_mfma_f32_16x16x32_f16 %0, %2, %3, %0\n\t"
+                         "v_mfma_f32_16x16x32_f16 %1, %2, %4, %1"
+                         : "+a"(acc[c][0]), "+a"(acc[c][1])
+                         : "v"(av), "v"(pk[kk][0]), "v"(pk[kk][1]));
+          else
+            asm volatile("s_nop 1\n\t"
+                         "v_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
+                         : "+a"(acc[c][0])
+                         : "v"(av), "v"(pk[kk][0]));
           __builtin_amdgcn_sched_barrier(0);
         });
       }
@@ -513,30 +548,30 @@ void latent_partial_kernel(LatArgs a) {
     // states; the compiler does not see the matrix-core writes in the asm)
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     // ---- partial of this fragment -------------------------------------------
-    float* part0 = part_of(s, 0);
-    float* part1 = part_of(s, 1);
-    l0 += shfl_xor_f32(l0, 16);
-    l1 += shfl_xor_f32(l1, 16);
-    l0 += shfl_xor_f32(l0, 32);
-    l1 += shfl_xor_f32(l1, 32);
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      l[ht] += shfl_xor_f32(l[ht], 16);
+      l[ht] += shfl_xor_f32(l[ht], 32);
+    }
     const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
     if (any_bad) {
       if (g == 0) {
-        part0[kDv] = __builtin_nanf("");
-        part1[kDv] = __builtin_nanf("");
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) prow[ht][kDv] = __builtin_nanf("");
       }
     } else {
       // acc[c][ht] register r: dim 16c + 4g + r of head 16 ht + n
 #pragma unroll
-      for (int c = 0; c < kDTiles; ++c) {
-        *reinterpret_cast<f32x4_t*>(part0 + 16 * c + 4 * g) = acc[c][0];
-        *reinterpret_cast<f32x4_t*>(part1 + 16 * c + 4 * g) = acc[c][1];
-      }
+      for (int c = 0; c < kDTiles; ++c)
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+          *reinterpret_cast<f32x4_t*>(prow[ht] + 16 * c + 4 * g) = acc[c][ht];
       if (g == 0) {
-        part0[kDv] = m0;
-        part0[kDv + 1] = l0;
-        part1[kDv] = m1;
-        part1[kDv + 1] = l1;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+          prow[ht][kDv] = m[ht];
+          prow[ht][kDv + 1] = l[ht];
+        }
       }
     }
     gp = pref[s] + j1;
@@ -609,18 +644,23 @@ size_t lat_slot_bytes(const pda_attn_shape& sh) {
 }
 
 size_t lat_lds_bytes(int B) {
-  return 2 * sizeof(PageBuf) + (size_t)kMaxWaves * kQLdsWave +
-         (size_t)(kThreadsL + 1 + B + 1) * sizeof(int);
+  return 2 * sizeof(PageBuf) + (size_t)kMaxTilesL * kQLdsTile +
+         (size_t)(kMaxThreadsL + 1 + B + 1) * sizeof(int);
 }
 
 typedef void (*lat_kernel_t)(LatArgs);
 
+// 16 heads per wave, two waves per SIMD at 128 heads (one wave of 32 heads
+// per SIMD, HT = 2, measured 4 % slower on 64 sequences x 128 heads)
+constexpr int kHT = 1;
+constexpr int kHeadsPerWave = 16 * kHT;
+
 lat_kernel_t pick_latent(int nw) {
   switch (nw) {
-    case 1: return latent_partial_kernel<1>;
-    case 2: return latent_partial_kernel<2>;
-    case 3: return latent_partial_kernel<3>;
-    default: return latent_partial_kernel<4>;
+    case 2: return latent_partial_kernel<2, kHT>;
+    case 4: return latent_partial_kernel<4, kHT>;
+    case 6: return latent_partial_kernel<6, kHT>;
+    default: return latent_partial_kernel<8, kHT>;
   }
 }
 
@@ -632,7 +672,7 @@ bool latent_supported(const pda_attn_shape& sh) {
   return sh.v_in_k == 1 && sh.kv_dtype == PDA_KV_FP8_E4M3 &&
          sh.scale_mode == PDA_SCALE_PER_TOKEN && sh.num_kv_heads == 1 &&
          sh.head_dim_qk == kDk && sh.head_dim_v == kDv && sh.page_size == kS &&
-         sh.num_q_heads % kHeadsPerWave == 0 && sh.num_q_heads <= kHeadsPerWave * kMaxWaves &&
+         sh.num_q_heads % 32 == 0 && sh.num_q_heads <= 128 &&
          sh.num_seqs <= kMaxSeqsL;
 }
 
@@ -675,7 +715,7 @@ int latent_launch(const pda_attn_shape& sh, const void* q, const void* k_cache,
   const int nw = sh.num_q_heads / kHeadsPerWave;
   const size_t lds = lat_lds_bytes(sh.num_seqs);
   lat_kernel_t k = pick_latent(nw);
-  static std::once_flag once[kMaxWaves];
+  static std::once_flag once[kMaxWavesL];
   bool attr_ok = true;
   std::call_once(once[nw - 1], [&] {
     attr_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
