@@ -1240,6 +1240,7 @@ extern "C" size_t paged_decode_attn_workspace_bytes(const pda_attn_shape* shape,
   if (max_seq_len < 0) return 0;
   const pda_attn_shape& sh = *shape;
   if (latent_supported(sh)) return latent_workspace_bytes(sh, max_seq_len);
+  if (!valu_supported(sh)) return 0;
   const int chunk = resolve_chunk(sh, max_seq_len);
   const long long ml = max_seq_len > 0 ? max_seq_len : 1;
   // units per sequence: chunks in groups of kWaves (one merged partial each)

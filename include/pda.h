@@ -186,10 +186,13 @@ int validate_page_tags(const uint32_t* page_tags, int32_t num_pages,
  * chunk count of a sequence divided by four and rounded up; a smaller
  * workspace down to one partial per (sequence, kv head) is still accepted,
  * and the device then widens the split chunk (by doubling) until the
- * partials fit, which changes results only within rounding. Latent path: a header plus one partial (Hq rows of Dv + 4
- * fp32) per (compute unit + sequence) of the current device; with less room
+ * partials fit, which changes results only within rounding. Latent path:
+ * a header plus one partial (Hq rows of Dv + 4 fp32) per (compute unit +
+ * sequence) of the current device; with less room
  * fewer workgroups are launched (at least one partial per sequence plus one
- * is required). Returns 0 for an invalid shape.
+ * is required). Returns 0 for an invalid shape and for a valid one that
+ * neither kernel supports (paged_decode_attn returns PDA_ERR_UNSUPPORTED
+ * for it).
  */
 size_t paged_decode_attn_workspace_bytes(const pda_attn_shape* shape,
                                          int32_t max_seq_len);

@@ -72,12 +72,21 @@ def test_workspace_sizes(pda):
         assert pda.paged_decode_attn_workspace_bytes(_shape(pda, **bad), 8192) == 0, bad
     assert pda.paged_decode_attn_workspace_bytes(sh, -1) == 0
     # latent path: one partial of 128 x (512 + 4) fp32 per (workgroup + sequence)
-    lat = _shape(pda, num_q_heads=128, num_kv_heads=1, head_dim_qk=576, head_dim_v=512,
-                 page_size=64, kv_dtype=pda.KV_FP8_E4M3, scale_mode=pda.SCALE_PER_TOKEN,
-                 v_in_k=True, split_tokens=0, sm_scale=1.0 / 24)
+    lat_kw = dict(num_q_heads=128, num_kv_heads=1, head_dim_qk=576, head_dim_v=512,
+                  page_size=64, kv_dtype=pda.KV_FP8_E4M3, scale_mode=pda.SCALE_PER_TOKEN,
+                  v_in_k=True, split_tokens=0, sm_scale=1.0 / 24)
+    lat = _shape(pda, **lat_kw)
     n = pda.paged_decode_attn_workspace_bytes(lat, 32768)
     slot = 128 * 516 * 4
     assert n > 0 and (n - 768) % slot == 0 and (n - 768) // slot > 64
+    # the latent kernel takes 32, 64, 96 or 128 heads and at most 2048 sequences
+    for hq in (32, 64, 96):
+        assert pda.paged_decode_attn_workspace_bytes(_shape(pda, **{**lat_kw, "num_q_heads": hq}),
+                                                     32768) > 0, hq
+    for bad in (dict(num_q_heads=48), dict(num_q_heads=160), dict(num_seqs=2049)):
+        assert pda.paged_decode_attn_workspace_bytes(_shape(pda, **{**lat_kw, **bad}), 32768) == 0, bad
+    assert pda.paged_decode_attn_workspace_bytes(_shape(pda, **{**lat_kw, "num_seqs": 2048}),
+                                                 32768) > 0
 
 
 def test_argument_checks_return_before_launch(pda):
