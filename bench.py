@@ -116,6 +116,48 @@ def time_steps(db, steps, warmup, torch):
                 attn_ms_max=max(att))
 
 
+def time_transcode(bf, fp8, args, torch, np, pda, reps=50):
+    """kv_transcode_bf16_to_fp8 of every page of the BF16 pool into a fresh
+    FP8 pool of the same size through a seeded permutation, timed with HIP
+    events on the launch stream over `reps` calls after a few warm-up calls.
+    Algorithmic bytes: BF16 K+V read, FP8 K+V written, 12 bytes of page
+    arrays per page."""
+    cfg = bf.cfg
+    S, P, hkv = cfg.page_size, bf.batch.num_pages, cfg.num_kv_heads
+    dk, dv = cfg.head_dim_qk, cfg.head_dim_v
+    rng = np.random.default_rng(77)
+    src = torch.arange(P, dtype=torch.int32, device="cuda")
+    dst = torch.from_numpy(rng.permutation(P).astype(np.int32)).cuda()
+    valid = torch.full((P,), S, dtype=torch.int32, device="cuda")
+    kd = torch.empty(P * hkv * S * dk, dtype=torch.uint8, device="cuda")
+    vd = torch.empty(P * hkv * S * dv, dtype=torch.uint8, device="cuda")
+
+    def call():
+        pda.kv_transcode_bf16_to_fp8(
+            bf.k_cache, bf.v_cache, src, dst, valid, kd, vd, num_kv_heads=hkv, head_dim_k=dk,
+            head_dim_v=dv, page_size=S, src_num_pages=P, dst_num_pages=P,
+            scale_mode=pda.SCALE_PER_HEAD, k_scale=fp8.k_scale, v_scale=fp8.v_scale)
+
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    nbytes = P * hkv * S * (dk + dv) * (2 + 1) + 12 * P
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    log(f"transcode of {P} pages: {ms:.4f} ms, {gbps:.0f} GB/s")
+    return {"pages": P, "ms": ms, "algorithmic_bytes_per_launch": nbytes,
+            "roofline": {"kernel": "kv_transcode_head_kernel", "bound": "hbm",
+                         "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": gbps / HBM_PEAK_GBPS}}
+
+
 def cpu_baseline(batch, data, host_scales, target_s=12.0):
     """The oracle (fp64, plain loops, all host threads) running the same
     step on whole sequences of the workload: kv write of the newest token,
@@ -273,6 +315,8 @@ def main():
             "seq_steps_per_s": B / (r16["step_ms"] * 1e-3),
             "step_ms": r16["step_ms"], "attn_ms": r16["attn_ms"],
             "validate_ms": r16["validate_ms"], "kv_write_ms": r16["kv_write_ms"]}
+        log("timing the BF16 -> FP8 page transcode of the whole pool")
+        res_bf16["transcode"] = time_transcode(bf, fp8, args, torch, np, pda)
         del bf
         torch.cuda.empty_cache()
 

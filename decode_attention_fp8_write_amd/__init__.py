@@ -22,7 +22,7 @@ PDA_OK, PDA_ERR_INVALID_ARG, PDA_ERR_UNSUPPORTED, PDA_ERR_LAUNCH, PDA_ERR_WORKSP
 KV_BF16, KV_FP8_E4M3 = 0, 1
 SCALE_NONE, SCALE_PER_HEAD, SCALE_PER_TOKEN = 0, 1, 2
 
-EXPORTS = ("kv_write_fp8", "kv_write_bf16", "validate_page_tags",
+EXPORTS = ("kv_write_fp8", "kv_write_bf16", "kv_transcode_bf16_to_fp8", "validate_page_tags",
            "paged_decode_attn_workspace_bytes", "paged_decode_attn",
            "pda_status_string")
 
@@ -63,6 +63,9 @@ def load(path: str | None = None):
     lib.kv_write_fp8.restype = ctypes.c_int
     lib.kv_write_bf16.argtypes = [V, V, I64P, I32, I32, I32, I32, I32, I32, V, V, V]
     lib.kv_write_bf16.restype = ctypes.c_int
+    lib.kv_transcode_bf16_to_fp8.argtypes = [V, V, V, V, V, I32, I32, I32, I32, I32, I32,
+                                             I32, I32, V, V, V, V, V, V]
+    lib.kv_transcode_bf16_to_fp8.restype = ctypes.c_int
     lib.validate_page_tags.argtypes = [V, I32, V, V, I32, V, I32, I32, V, V]
     lib.validate_page_tags.restype = ctypes.c_int
     lib.paged_decode_attn_workspace_bytes.argtypes = [ctypes.POINTER(AttnShape), I32]
@@ -131,6 +134,26 @@ def kv_write_bf16(k_new, v_new, slot_mapping, k_cache, v_cache, *, page_size, nu
         _ptr(k_cache, elem=2, name="k_cache"), _ptr(v_cache, elem=2, name="v_cache"),
         _stream(stream))
     _check("kv_write_bf16", st)
+
+
+def kv_transcode_bf16_to_fp8(k_src, v_src, src_pages, dst_pages, valid, k_dst, v_dst, *,
+                             num_kv_heads, head_dim_k, head_dim_v, page_size, src_num_pages,
+                             dst_num_pages, scale_mode=SCALE_PER_HEAD, k_scale=None,
+                             v_scale=None, token_scale=None, stream=None):
+    """Re-encode slots [0, valid[i]) of BF16 page src_pages[i] into FP8 page
+    dst_pages[i] (int32 device arrays of one length; caches as in
+    include/pda.h: uint16 sources, uint8 destinations)."""
+    n = src_pages.numel()
+    if dst_pages.numel() != n or valid.numel() != n:
+        raise ValueError("src_pages, dst_pages and valid must have one length")
+    st = load().kv_transcode_bf16_to_fp8(
+        _ptr(k_src, elem=2, name="k_src"), _ptr(v_src, elem=2, name="v_src"),
+        _ptr(src_pages, elem=4, name="src_pages"), _ptr(dst_pages, elem=4, name="dst_pages"),
+        _ptr(valid, elem=4, name="valid"), n, num_kv_heads, head_dim_k, head_dim_v, page_size,
+        src_num_pages, dst_num_pages, scale_mode, _ptr(k_scale, elem=4, name="k_scale"),
+        _ptr(v_scale, elem=4, name="v_scale"), _ptr(token_scale, elem=4, name="token_scale"),
+        _ptr(k_dst, elem=1, name="k_dst"), _ptr(v_dst, elem=1, name="v_dst"), _stream(stream))
+    _check("kv_transcode_bf16_to_fp8", st)
 
 
 def validate_page_tags(page_tags, block_table, expected_tags, seq_lens, verdict, *,

@@ -979,7 +979,6 @@ void attn_partial_kernel(AttnArgs a) {
       if ((long long)(pref[mid] / kWaves) * a.Hkv <= u) lo = mid; else hi = mid;
     }
     const int s = __builtin_amdgcn_readfirstlane(lo);
-    const int ncq = (pref[s + 1] - pref[s]) / kWaves;
     const int local = (int)(u - (long long)(pref[s] / kWaves) * a.Hkv);
     const int g = __builtin_amdgcn_readfirstlane(local % a.Hkv);
     const int j = local / a.Hkv;   // unit of (s, g)

@@ -149,6 +149,132 @@ __global__ __launch_bounds__(kThreads) void kv_write_bf16_kernel(
   }
 }
 
+// ---- BF16 -> FP8 page transcode ---------------------------------------------
+// Both formats share the element order, so a (page, head) block of either
+// cache is S*Dk (K) or S*Dv (V) consecutive elements and the transcode is
+// elementwise on matching indices: 8 elements (16 bytes in, 8 out) per step.
+
+// Slot of element e of a (page, head) block. K: rows of 16 dims per slot in
+// column groups of S rows. V: slot pairs interleaved element by element.
+__device__ __forceinline__ int k_slot(int e, int S) { return (e >> 4) % S; }
+__device__ __forceinline__ int v_slot(int e, int dv) { return 2 * (e / (2 * dv)) + (e & 1); }
+
+__device__ __forceinline__ uint2 encode8(uint4 x, float sc) {
+  return make_uint2(e4m3x4(bf16_lo(x.x) / sc, bf16_hi(x.x) / sc, bf16_lo(x.y) / sc,
+                           bf16_hi(x.y) / sc),
+                    e4m3x4(bf16_lo(x.z) / sc, bf16_hi(x.z) / sc, bf16_lo(x.w) / sc,
+                           bf16_hi(x.w) / sc));
+}
+
+__device__ __forceinline__ bool pair_ok(int src, int dst, int n, int ps, int pd, int S) {
+  return src >= 0 && src < ps && dst >= 0 && dst < pd && n >= 0 && n <= S;
+}
+
+// One workgroup per pair, per-head scales: the page's blocks of all kv heads
+// are contiguous (Hkv*S*Dk K elements, then Hkv*S*Dv V elements), each
+// thread takes 8 elements per step, four steps' loads issued before their
+// conversions and stores.
+template <bool V>
+__device__ __forceinline__ void transcode_span(const uint16_t* __restrict__ src,
+                                               uint8_t* __restrict__ dst, int n_elems,
+                                               int head_elems, int S, int D, int valid,
+                                               const float* __restrict__ scale) {
+  constexpr int U = 4;
+  for (int e0 = threadIdx.x * 8; e0 < n_elems; e0 += kThreads * 8 * U) {
+    uint4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = e0 + u * kThreads * 8;
+      if (e < n_elems) x[u] = *reinterpret_cast<const uint4*>(src + e);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = e0 + u * kThreads * 8;
+      if (e >= n_elems) break;
+      const int h = e / head_elems;
+      const int eh = e - h * head_elems;
+      const int s0 = V ? v_slot(eh, D) : k_slot(eh, S);
+      if (s0 >= valid) continue;
+      const uint2 c = encode8(x[u], scale[h]);
+      if (!V || s0 + 1 < valid) {
+        *reinterpret_cast<uint2*>(dst + e) = c;
+      } else {   // only the even slot of a V pair: its four bytes
+        uint8_t* d = dst + e;
+        d[0] = (uint8_t)c.x;
+        d[2] = (uint8_t)(c.x >> 16);
+        d[4] = (uint8_t)c.y;
+        d[6] = (uint8_t)(c.y >> 16);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void kv_transcode_head_kernel(
+    const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src,
+    const int32_t* __restrict__ src_pages, const int32_t* __restrict__ dst_pages,
+    const int32_t* __restrict__ valid, int hkv, int dk, int dv, int S, int ps, int pd,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+    uint8_t* __restrict__ k_dst, uint8_t* __restrict__ v_dst) {
+  const int pair = blockIdx.x;
+  const int src = src_pages[pair], dst = dst_pages[pair], n = valid[pair];
+  if (!pair_ok(src, dst, n, ps, pd, S) || n == 0) return;
+  const int nk = hkv * S * dk;
+  transcode_span<false>(k_src + (int64_t)src * nk, k_dst + (int64_t)dst * nk, nk, S * dk, S,
+                        dk, n, k_scale);
+  if (v_src == nullptr) return;
+  const int nv = hkv * S * dv;
+  transcode_span<true>(v_src + (int64_t)src * nv, v_dst + (int64_t)dst * nv, nv, S * dv, S, dv,
+                       n, v_scale);
+}
+
+// One workgroup per pair, latent cache (Hkv == 1, K only), per-token scales:
+// thread (slot t, quarter q) handles column groups q, q+4, ... of slot t.
+__global__ __launch_bounds__(kThreads) void kv_transcode_token_kernel(
+    const uint16_t* __restrict__ k_src, const int32_t* __restrict__ src_pages,
+    const int32_t* __restrict__ dst_pages, const int32_t* __restrict__ valid, int dk, int S,
+    int ps, int pd, float* __restrict__ token_scale, uint8_t* __restrict__ k_dst) {
+  __shared__ float red[kThreads];
+  const int pair = blockIdx.x;
+  const int src = src_pages[pair], dst = dst_pages[pair], n = valid[pair];
+  if (!pair_ok(src, dst, n, ps, pd, S) || n == 0) return;
+  const int64_t sb = (int64_t)src * S * dk;
+  const int64_t db = (int64_t)dst * S * dk;
+  const int groups = dk / 16;
+  const int per = kThreads / S;   // threads per slot (S divides kThreads)
+  for (int t0 = 0; t0 < S; t0 += kThreads / per) {
+    const int t = t0 + threadIdx.x % (kThreads / per);
+    const int q = threadIdx.x / (kThreads / per);
+    const bool live = t < S && t < n;
+    float amax = 0.0f;   // NaN values are ignored (fmaxf)
+    if (live)
+      for (int c = q; c < groups; c += per) {
+        const uint16_t* x = k_src + sb + ((int64_t)c * S + t) * 16;
+        const uint4 a = *reinterpret_cast<const uint4*>(x);
+        const uint4 b = *reinterpret_cast<const uint4*>(x + 8);
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+      }
+    red[threadIdx.x] = amax;
+    __syncthreads();
+    if (live) {
+      float m = 0.0f;
+      for (int i = 0; i < per; ++i) m = fmaxf(m, red[i * (kThreads / per) + threadIdx.x % (kThreads / per)]);
+      const float sc = (m > 0.0f) ? m / 448.0f : 1.0f;
+      if (q == 0) token_scale[(int64_t)dst * S + t] = sc;
+      for (int c = q; c < groups; c += per) {
+        const int64_t o = ((int64_t)c * S + t) * 16;
+        const uint4 a = *reinterpret_cast<const uint4*>(k_src + sb + o);
+        const uint4 b = *reinterpret_cast<const uint4*>(k_src + sb + o + 8);
+        const uint2 ca = encode8(a, sc), cb = encode8(b, sc);
+        *reinterpret_cast<uint4*>(k_dst + db + o) = make_uint4(ca.x, ca.y, cb.x, cb.y);
+      }
+    }
+    __syncthreads();   // red is reused by the next round of slots
+  }
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 int check_common(const void* k_new, const void* v_new, const int64_t* slots, int32_t T,
@@ -217,5 +343,49 @@ extern "C" int kv_write_bf16(const void* k_new, const void* v_new, const int64_t
                      static_cast<const uint16_t*>(v_new), slot_mapping, num_kv_heads, head_dim_k,
                      head_dim_v, page_size, num_pages, static_cast<uint16_t*>(k_cache),
                      static_cast<uint16_t*>(v_cache));
+  return launch_status();
+}
+
+extern "C" int kv_transcode_bf16_to_fp8(const void* k_src, const void* v_src,
+                                        const int32_t* src_pages, const int32_t* dst_pages,
+                                        const int32_t* valid, int32_t num_pairs,
+                                        int32_t num_kv_heads, int32_t head_dim_k,
+                                        int32_t head_dim_v, int32_t page_size,
+                                        int32_t src_num_pages, int32_t dst_num_pages,
+                                        int32_t scale_mode, const float* k_scale,
+                                        const float* v_scale, float* token_scale,
+                                        uint8_t* k_dst, uint8_t* v_dst, void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || head_dim_k <= 0 || page_size <= 0 ||
+      src_num_pages <= 0 || dst_num_pages <= 0)
+    return PDA_ERR_INVALID_ARG;
+  if (num_pairs > 0 && (!src_pages || !dst_pages || !valid)) return PDA_ERR_INVALID_ARG;
+  if (!k_src || !k_dst) return PDA_ERR_INVALID_ARG;
+  const bool latent = (v_src == nullptr);
+  if (latent != (v_dst == nullptr)) return PDA_ERR_INVALID_ARG;
+  if (head_dim_k % 16 != 0 || page_size % 2 != 0) return PDA_ERR_UNSUPPORTED;
+  if (!latent && (head_dim_v <= 0 || head_dim_v % 8 != 0)) return PDA_ERR_UNSUPPORTED;
+  if (!aligned(k_src, 16) || (!latent && !aligned(v_src, 16)) || !aligned(k_dst, 16) ||
+      (!latent && !aligned(v_dst, 8)))
+    return PDA_ERR_INVALID_ARG;
+  if (scale_mode == PDA_SCALE_PER_HEAD) {
+    if (!k_scale || (!latent && !v_scale) || token_scale) return PDA_ERR_INVALID_ARG;
+  } else if (scale_mode == PDA_SCALE_PER_TOKEN) {
+    if (!token_scale || k_scale || v_scale) return PDA_ERR_INVALID_ARG;
+    if (!latent || num_kv_heads != 1) return PDA_ERR_UNSUPPORTED;
+    if (kThreads % page_size != 0) return PDA_ERR_UNSUPPORTED;
+  } else {
+    return PDA_ERR_INVALID_ARG;
+  }
+  if (num_pairs == 0) return PDA_OK;
+  hipStream_t s = as_stream(stream);
+  if (scale_mode == PDA_SCALE_PER_TOKEN)
+    hipLaunchKernelGGL(kv_transcode_token_kernel, dim3(num_pairs), dim3(kThreads), 0, s,
+                       static_cast<const uint16_t*>(k_src), src_pages, dst_pages, valid,
+                       head_dim_k, page_size, src_num_pages, dst_num_pages, token_scale, k_dst);
+  else
+    hipLaunchKernelGGL(kv_transcode_head_kernel, dim3((unsigned)num_pairs), dim3(kThreads), 0, s, static_cast<const uint16_t*>(k_src),
+                       static_cast<const uint16_t*>(v_src), src_pages, dst_pages, valid,
+                       num_kv_heads, head_dim_k, head_dim_v, page_size, src_num_pages,
+                       dst_num_pages, k_scale, v_scale, k_dst, v_dst);
   return launch_status();
 }

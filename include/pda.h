@@ -116,7 +116,8 @@ typedef struct pda_attn_shape {
  *               token_scale must be NULL.
  *               PER_TOKEN (latent caches only: Hkv == 1, v_new == NULL):
  *               the call computes sc = amax/448 (fp32 division; amax = max
- *               |x| over the token's Dk values; 1.0 when amax == 0) and writes
+ *               |x| over the token's Dk values, NaN values (quiet or
+ *               signaling) ignored; 1.0 when amax == 0) and writes
  *               it to token_scale[slot]; k_scale/v_scale must be NULL.
  *  Per element: code = e4m3(fp32(x) / scale), the division correctly rounded
  *               in fp32, then round-to-nearest-even with saturation to ±448
@@ -143,6 +144,46 @@ int kv_write_bf16(const void* k_new, const void* v_new,
                   int32_t num_kv_heads, int32_t head_dim_k, int32_t head_dim_v,
                   int32_t page_size, int32_t num_pages,
                   void* k_cache, void* v_cache, void* stream);
+
+/*
+ * kv_transcode_bf16_to_fp8 — re-encode pages of a BF16 cache as pages of an
+ * FP8 e4m3 cache. The pages describe separate GPU pools for prefill and
+ * decode, the prefill pool keeping its cache in BF16 and the decode pool in
+ * FP8 ([SK] § "Kompresia sa oplatí inde pri vstupe a inde pri výstupe"; [VN]
+ * § "Bộ nhớ đệm KV FP8 tăng gấp đôi dung lượng ngữ cảnh"; [DE] § "Was
+ * Cloudflare für Kimi und GLM geändert hat"; [JA] § "並行性を高めるための KV
+ * キャッシュ量子化"), so a request's pages change format when it moves from
+ * the first pool to the second. They do not say how; the reading taken
+ * here is that every token is quantised exactly as kv_write_fp8 would have
+ * quantised the same BF16 rows in the decode pool.
+ *
+ *  k_src, v_src BF16 caches (uint16 elements) in the format above, with
+ *               src_num_pages pages; v_src NULL iff the caches are latent
+ *               (then v_dst must be NULL too and Dv is ignored).
+ *  src_pages, dst_pages, valid  int32 [num_pairs] device arrays: pair i
+ *               re-encodes slots [0, valid[i]) of BF16 page src_pages[i]
+ *               into the same slots of FP8 page dst_pages[i]. A pair whose
+ *               page ids fall outside [0, src_num_pages) / [0, dst_num_pages)
+ *               or whose valid lies outside [0, page_size] writes nothing.
+ *               Two pairs with the same destination page are undefined.
+ *  scale_mode   PER_HEAD: k_scale[Hkv], v_scale[Hkv] fp32 inputs, token_scale
+ *               NULL. PER_TOKEN (latent, Hkv == 1): the per-token scale of
+ *               every re-encoded slot is computed as kv_write_fp8 computes it
+ *               and written to token_scale[dst_page*page_size + slot].
+ *  k_dst, v_dst FP8 caches with dst_num_pages pages. Slots at or past
+ *               valid[i], and pages no pair names, are left unchanged.
+ *  Errors as kv_write_fp8 (page_size must also divide into whole 16-dim
+ *  column groups: Dk % 16 == 0; even page_size; Dv % 8 == 0 unless latent).
+ */
+int kv_transcode_bf16_to_fp8(const void* k_src, const void* v_src,
+                             const int32_t* src_pages, const int32_t* dst_pages,
+                             const int32_t* valid, int32_t num_pairs,
+                             int32_t num_kv_heads, int32_t head_dim_k,
+                             int32_t head_dim_v, int32_t page_size,
+                             int32_t src_num_pages, int32_t dst_num_pages,
+                             int32_t scale_mode, const float* k_scale,
+                             const float* v_scale, float* token_scale,
+                             uint8_t* k_dst, uint8_t* v_dst, void* stream);
 
 /*
  * validate_page_tags — the separate batched check of cache-page tags that

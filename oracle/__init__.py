@@ -58,6 +58,9 @@ def _load():
     lib.oracle_kv_write_bf16.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32,
                                          P, P]
     lib.oracle_kv_write_bf16.restype = ctypes.c_int
+    lib.oracle_kv_transcode_bf16_to_fp8.argtypes = [P, P, P, P, P, i32, i32, i32, i32,
+                                                    i32, i32, i32, i32, P, P, P, P, P]
+    lib.oracle_kv_transcode_bf16_to_fp8.restype = ctypes.c_int
     lib.oracle_validate_page_tags.argtypes = [P, i32, P, P, i32, P, i32, i32, P]
     lib.oracle_validate_page_tags.restype = None
     lib.oracle_paged_decode_attn.argtypes = [
@@ -142,6 +145,29 @@ def kv_write_bf16(k_new, v_new, slot_mapping, page_size, num_pages, k_cache,
         num_pages, _ptr(k_cache), _ptr(v_cache))
     if rc != 0:
         raise ValueError("oracle_kv_write_bf16 rejected its arguments")
+
+
+def kv_transcode_bf16_to_fp8(k_src, v_src, src_pages, dst_pages, valid, num_kv_heads,
+                             head_dim_k, head_dim_v, page_size, src_num_pages,
+                             dst_num_pages, scale_mode, k_scale, v_scale, token_scale,
+                             k_dst, v_dst):
+    """In place: re-encode slots [0, valid[i]) of BF16 page src_pages[i] into
+    FP8 page dst_pages[i] (uint16 / uint8 numpy caches, flat)."""
+    k_src = _arr(k_src, np.uint16)
+    v_src = _arr(v_src, np.uint16)
+    sp = _arr(np.asarray(src_pages, np.int32), np.int32)
+    dp = _arr(np.asarray(dst_pages, np.int32), np.int32)
+    vl = _arr(np.asarray(valid, np.int32), np.int32)
+    for c in (k_dst, v_dst, token_scale):
+        if c is not None:
+            assert c.flags["C_CONTIGUOUS"]
+    rc = _load().oracle_kv_transcode_bf16_to_fp8(
+        _ptr(k_src), _ptr(v_src), _ptr(sp), _ptr(dp), _ptr(vl), len(sp), num_kv_heads,
+        head_dim_k, head_dim_v, page_size, src_num_pages, dst_num_pages, scale_mode,
+        _ptr(_arr(k_scale, np.float32)), _ptr(_arr(v_scale, np.float32)), _ptr(token_scale),
+        _ptr(k_dst), _ptr(v_dst))
+    if rc != 0:
+        raise ValueError("oracle_kv_transcode_bf16_to_fp8 rejected its arguments")
 
 
 # --- validation ---------------------------------------------------------------

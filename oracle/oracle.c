@@ -136,7 +136,9 @@ int oracle_kv_write_fp8(const uint16_t* k_new, const uint16_t* v_new,
       float amax = 0.0f;
       for (int32_t d = 0; d < dk; ++d) {
         float a = fabsf(oracle_bf16_to_f32(k_new[(size_t)t * dk + d]));
-        amax = fmaxf(amax, a); /* NaN inputs are ignored (fmax semantics) */
+        /* NaN inputs, quiet or signaling, are ignored (C's fmaxf would let a
+         * signaling NaN reset the running maximum) */
+        if (!isnan(a) && a > amax) amax = a;
       }
       tok_sc = (amax > 0.0f) ? amax / 448.0f : 1.0f;
       token_scale[slot] = tok_sc;
@@ -186,6 +188,50 @@ int oracle_kv_write_bf16(const uint16_t* k_new, const uint16_t* v_new,
     }
   }
   return 0;
+}
+
+/* Page transcode BF16 -> FP8 between the prefill pool's BF16 cache and the
+ * decode pool's FP8 cache ([SK] § "Kompresia sa oplatí inde pri vstupe a
+ * inde pri výstupe"; [VN] § "Bộ nhớ đệm KV FP8 tăng gấp đôi dung lượng ngữ
+ * cảnh"). Definition (the reading of include/pda.h): read each re-encoded
+ * slot's BF16 rows back out of the source cache and write them with
+ * oracle_kv_write_fp8 to the same slot of the destination page. */
+int oracle_kv_transcode_bf16_to_fp8(
+    const uint16_t* k_src, const uint16_t* v_src, const int32_t* src_pages,
+    const int32_t* dst_pages, const int32_t* valid, int32_t num_pairs,
+    int32_t hkv, int32_t dk, int32_t dv, int32_t s, int32_t src_num_pages,
+    int32_t dst_num_pages, int32_t scale_mode, const float* k_scale,
+    const float* v_scale, float* token_scale, uint8_t* k_dst,
+    uint8_t* v_dst) {
+  int latent = (v_src == NULL);
+  if (num_pairs < 0 || src_num_pages <= 0) return -1;
+  if (!kv_args_ok(num_pairs, hkv, dk, dv, s, dst_num_pages, latent)) return -1;
+  if (latent != (v_dst == NULL)) return -1;
+  uint16_t* krow = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)hkv * dk);
+  uint16_t* vrow = latent ? NULL : (uint16_t*)malloc(sizeof(uint16_t) * (size_t)hkv * dv);
+  int rc = 0;
+  for (int32_t i = 0; i < num_pairs && rc == 0; ++i) {
+    int32_t src = src_pages[i], dst = dst_pages[i], n = valid[i];
+    if (src < 0 || src >= src_num_pages || dst < 0 || dst >= dst_num_pages ||
+        n < 0 || n > s)
+      continue;
+    for (int32_t off = 0; off < n && rc == 0; ++off) {
+      for (int32_t h = 0; h < hkv; ++h) {
+        for (int32_t d = 0; d < dk; ++d)
+          krow[(size_t)h * dk + d] = k_src[k_index(src, h, off, d, hkv, dk, s)];
+        if (!latent)
+          for (int32_t d = 0; d < dv; ++d)
+            vrow[(size_t)h * dv + d] = v_src[v_index(src, h, off, d, hkv, dv, s)];
+      }
+      int64_t slot = (int64_t)dst * s + off;
+      rc = oracle_kv_write_fp8(krow, vrow, &slot, 1, hkv, dk, dv, s,
+                               dst_num_pages, scale_mode, k_scale, v_scale,
+                               token_scale, k_dst, v_dst);
+    }
+  }
+  free(krow);
+  free(vrow);
+  return rc;
 }
 
 /* ------------------------------------------------------------------------ */

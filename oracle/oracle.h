@@ -66,6 +66,17 @@ int oracle_kv_write_bf16(const uint16_t* k_new, const uint16_t* v_new,
                          int32_t num_pages, uint16_t* k_cache,
                          uint16_t* v_cache);
 
+/* Page transcode: same argument meaning as kv_transcode_bf16_to_fp8 in
+ * include/pda.h, with host arrays. Returns 0, or -1 for arguments the GPU
+ * call rejects. */
+int oracle_kv_transcode_bf16_to_fp8(
+    const uint16_t* k_src, const uint16_t* v_src, const int32_t* src_pages,
+    const int32_t* dst_pages, const int32_t* valid, int32_t num_pairs,
+    int32_t num_kv_heads, int32_t head_dim_k, int32_t head_dim_v,
+    int32_t page_size, int32_t src_num_pages, int32_t dst_num_pages,
+    int32_t scale_mode, const float* k_scale, const float* v_scale,
+    float* token_scale, uint8_t* k_dst, uint8_t* v_dst);
+
 /* --- page-tag validation --------------------------------------------------
  * Verdict per sequence exactly as validate_page_tags documents it. */
 void oracle_validate_page_tags(const uint32_t* page_tags, int32_t num_pages,

@@ -28,7 +28,8 @@ def pda():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    assert names == sorted(["kv_write_fp8", "kv_write_bf16", "validate_page_tags",
+    assert names == sorted(["kv_write_fp8", "kv_write_bf16", "kv_transcode_bf16_to_fp8",
+                            "validate_page_tags",
                             "paged_decode_attn_workspace_bytes", "paged_decode_attn",
                             "pda_status_string"])
 
@@ -126,3 +127,33 @@ def test_argument_checks_return_before_launch(pda):
         pda.PDA_ERR_INVALID_ARG
     assert lib.validate_page_tags(null, 64, fake, fake, 16, fake, 4, 16, fake, null) == \
         pda.PDA_ERR_INVALID_ARG
+
+
+def test_transcode_argument_checks(pda):
+    lib = pda.load()
+    null = None
+    fake = ctypes.c_void_p(256)
+    # (k_src, v_src, src, dst, valid, n, hkv, dk, dv, S, Ps, Pd, mode, ks, vs, ts, kd, vd, stream)
+    ok = [fake, fake, fake, fake, fake, 4, 8, 128, 128, 16, 64, 64, pda.SCALE_PER_HEAD, fake,
+          fake, null, fake, fake, null]
+
+    def call(**kw):
+        args = list(ok)
+        names = ["k_src", "v_src", "src", "dst", "valid", "n", "hkv", "dk", "dv", "S", "Ps",
+                 "Pd", "mode", "ks", "vs", "ts", "kd", "vd", "stream"]
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return lib.kv_transcode_bf16_to_fp8(*args)
+
+    assert call(n=0) == pda.PDA_OK                          # nothing to do
+    assert call(n=-1) == pda.PDA_ERR_INVALID_ARG
+    assert call(src=null) == pda.PDA_ERR_INVALID_ARG
+    assert call(v_src=null) == pda.PDA_ERR_INVALID_ARG      # latent source, non-latent dest
+    assert call(dk=100) == pda.PDA_ERR_UNSUPPORTED
+    assert call(S=15) == pda.PDA_ERR_UNSUPPORTED
+    assert call(mode=7) == pda.PDA_ERR_INVALID_ARG
+    assert call(ts=fake) == pda.PDA_ERR_INVALID_ARG         # per-head takes no token scales
+    assert call(mode=pda.SCALE_PER_TOKEN, ks=null, vs=null, ts=fake) == \
+        pda.PDA_ERR_UNSUPPORTED                             # per-token needs a latent cache
+    assert call(k_src=ctypes.c_void_p(264)) == pda.PDA_ERR_INVALID_ARG   # misaligned
+    assert call(Ps=0) == pda.PDA_ERR_INVALID_ARG

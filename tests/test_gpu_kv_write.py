@@ -64,6 +64,8 @@ def test_per_token_latent_bit_exact(gpu):
     k = synth.bf16_from_f32(x)
     k[7] = 0                                    # amax 0 -> scale 1
     k[9, 0, :5] = 0x7FC0                        # NaN values are ignored by amax
+    k[11, 0, 3] = 0x7F81                        # signaling NaNs too, mid-row
+    k[12, 0, 400] = 0xFF81
     slots = rng.choice(P * S, T, replace=False).astype(np.int64)
     slots[3] = -1
     kc = np.full(P * S * dk, 0xA5, np.uint8)
