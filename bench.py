@@ -248,6 +248,47 @@ def other_workload(args, torch, np, synth, pda, workload):
     return line
 
 
+def sweep(args, torch, np, synth, pda, workload):
+    """Kernel-level concurrency and capacity sweep: B sequences of 8192
+    tokens (the 64 x 8192 workload's heads and outliers; automatic split-K,
+    which keeps 512-token chunks from 32 sequences up and halves them below
+    so that small batches still fill the chip) for B in 1, 8, 16, 32, 64,
+    FP8 and BF16 caches, each timed like the metric's workload; plus cache
+    bytes per token and tokens per GiB of pool."""
+    rows = []
+    for B in (1, 8, 16, 32, 64):
+        batch = synth.make_batch(WORKLOAD_ID, lens=[8192] * B)
+        cfg = batch.cfg
+        data = synth.map_seqs(lambda s: batch.kv(s), list(range(B)),
+                              min(16, os.cpu_count() or 1))
+        row = {"seqs": B}
+        for name, dt in (("fp8", pda.KV_FP8_E4M3), ("bf16", pda.KV_BF16)):
+            db = workload.build(batch, dt, data=data)
+            db.alloc_workspace(split_tokens=0)
+            log(f"sweep B={B} {name}")
+            r = time_steps(db, args.steps, args.warmup, torch)
+            kv = workload.kv_bytes(batch, dt)
+            row[name] = {"split": "auto", "step_ms": r["step_ms"], "attn_ms": r["attn_ms"],
+                         "seq_steps_per_s": B / (r["step_ms"] * 1e-3),
+                         "kv_GBps_attn": kv / (r["attn_ms"] * 1e-3) / 1e9,
+                         "pct_hbm_peak_attn": 100.0 * kv / (r["attn_ms"] * 1e-3) / 1e9
+                         / HBM_PEAK_GBPS}
+            del db
+            torch.cuda.empty_cache()
+        row["fp8_over_bf16_seq_steps"] = (row["fp8"]["seq_steps_per_s"]
+                                          / row["bf16"]["seq_steps_per_s"])
+        rows.append(row)
+        del data
+    cfg = synth.CONFIGS[WORKLOAD_ID]
+    per_tok = {"fp8": cfg.num_kv_heads * (cfg.head_dim_qk + cfg.head_dim_v),
+               "bf16": 2 * cfg.num_kv_heads * (cfg.head_dim_qk + cfg.head_dim_v)}
+    return {"metric": "kernel-level concurrency sweep, 8192-token contexts, FP8 vs BF16 KV",
+            "unit": "seq-steps/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "data": "synthetic", "rows": rows,
+            "capacity": {"cache_bytes_per_token": per_tok,
+                         "tokens_per_GiB": {k: (1 << 30) // v for k, v in per_tok.items()}}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,6 +299,9 @@ def main():
     ap.add_argument("--workload", type=int, default=WORKLOAD_ID, choices=(2, 3, 4, 5),
                     help="3 (default) is the metric's workload; 2, 4 and 5 print an extra "
                          "line for the other full-size workloads (4 = latent, matrix cores)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="kernel-level concurrency sweep: 1..64 sequences of 8192 tokens, "
+                         "FP8 and BF16; one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy, whose HBM "
                          "counters calibrate FETCH_SIZE / WRITE_SIZE in a profiled run")
@@ -287,6 +331,9 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
         log("copy calibration: 1 GiB read + 1 GiB written by one copy kernel")
+    if args.sweep:
+        print(json.dumps(sweep(args, torch, np, synth, pda, workload)), flush=True)
+        return
     if args.workload != WORKLOAD_ID:
         print(json.dumps(other_workload(args, torch, np, synth, pda, workload)), flush=True)
         return

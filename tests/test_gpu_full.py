@@ -98,3 +98,27 @@ def test_workload4_sampled(gpu):
     assert np.all(verdict == 0)
     mx, rel = assert_attn_close(got, ref, "workload 4")
     log(f"  workload 4: max_abs {mx:.3e} rel_l2 {rel:.3e}")
+
+
+@pytest.mark.parametrize("kv_dtype", [synth.KV_BF16, synth.KV_FP8])
+@pytest.mark.parametrize("B", [1, 8])
+def test_concurrency_sweep_shapes(gpu, B, kv_dtype):
+    """The smaller batches of the concurrency sweep (B sequences of 8192
+    tokens, the 64 x 8192 workload's heads and outliers, automatic split-K:
+    128-token chunks for 8 sequences, 64 for one), launched as bench.py
+    --sweep launches them; every sequence compared."""
+    from decode_attention_fp8_write_amd import workload
+    log(f"sweep shape B={B}, dtype {kv_dtype}")
+    b = synth.make_batch(3, lens=[8192] * B)
+    data = synth.map_seqs(lambda s: b.kv(s), list(range(B)), threads())
+    db = workload.build(b, kv_dtype, data=data)
+    db.alloc_workspace(split_tokens=0)
+    db.step(use_verdict=True)
+    torch.cuda.synchronize()
+    verdict = db.verdict.cpu().numpy()
+    assert np.all(verdict == 0)
+    got = db.out.cpu().numpy()
+    seqs = list(range(B))
+    sub = oracle_subset(b, data, seqs, kv_dtype, db.host_scales)
+    ref = oracle_attn_subset(b, sub, kv_dtype, db.host_scales, verdict=verdict)
+    assert_attn_close(got, ref, f"sweep B={B} dtype {kv_dtype}")
