@@ -116,6 +116,51 @@ def time_steps(db, steps, warmup, torch):
                 attn_ms_max=max(att))
 
 
+def time_plain_steps(db, steps, warmup, torch, use_verdict):
+    """Step time alone (events around exactly `steps` steps), with the tag
+    check (validate + verdict-gated attention) or without it (no validate
+    call, NULL verdict: the no-op tracker)."""
+    for _ in range(warmup):
+        db.step(use_verdict=use_verdict)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        db.step(use_verdict=use_verdict)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def time_page_pool(pda, np, seconds=0.3):
+    """Host page pool throughput: hand out and return the 512 pages of one
+    8192-token sequence (page 16) per cycle, tracking on and off, on a
+    32768-page pool (the 64 x 8192 workload's pool); plus the oracle's pool
+    (pure Python) for scale. Pages per second of alloc + free."""
+    from oracle.pool import OraclePagePool
+
+    def run(pool, alloc, free):
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            pages = alloc(pool)
+            free(pool, pages)
+            n += 512
+        return n / (time.perf_counter() - t0)
+
+    P = 32768
+    order = np.random.default_rng(1).permutation(P)
+    res = {}
+    for name, track in (("tags", True), ("no_op", False)):
+        pool = pda.PagePool(P, initial_order=order, track_tags=track)
+        res[f"native_{name}_pages_per_s"] = run(pool, lambda q: q.alloc(512)[0],
+                                                lambda q, p: q.free(p))
+        pool.close()
+    ref = OraclePagePool(P, initial_order=order)
+    res["oracle_pages_per_s"] = run(ref, lambda q: q.alloc(512)[0], lambda q, p: q.free(p))
+    return res
+
+
 def time_transcode(bf, fp8, args, torch, np, pda, reps=50):
     """kv_transcode_bf16_to_fp8 of every page of the BF16 pool into a fresh
     FP8 pool of the same size through a seeded permutation, timed with HIP
@@ -348,6 +393,15 @@ def main():
     r8 = time_steps(fp8, args.steps, args.warmup, torch)
     kv8 = workload.kv_bytes(batch, pda.KV_FP8_E4M3)
     B = batch.B
+    # tag-check overhead: the same steps with the no-op tracker, interleaved
+    # on/off passes so clock drift cancels
+    log("timing steps with and without the tag check")
+    on, off = [], []
+    for _ in range(3):
+        off.append(time_plain_steps(fp8, args.steps, 10, torch, use_verdict=False))
+        on.append(time_plain_steps(fp8, args.steps, 10, torch, use_verdict=True))
+    tracker = {"step_ms_check_on": min(on), "step_ms_check_off": min(off),
+               "overhead_frac": min(on) / min(off) - 1.0}
     res_bf16 = None
     if not args.no_bf16:
         log("building BF16 cache")
@@ -402,6 +456,8 @@ def main():
         "validate_ms": r8["validate_ms"],
         "kv_write_ms": r8["kv_write_ms"],
         "validate_frac_of_step": r8["validate_ms"] / r8["step_ms_with_call_events"],
+        "tag_check": tracker,
+        "page_pool": time_page_pool(pda, np),
         "step_ms_with_call_events": r8["step_ms_with_call_events"],
         "kv_GBps_attn": kv8 / attn_s / 1e9,
         "wall_ms_per_step": r8["wall_ms_per_step"],

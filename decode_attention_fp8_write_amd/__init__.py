@@ -18,13 +18,15 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpda.so")
 
-PDA_OK, PDA_ERR_INVALID_ARG, PDA_ERR_UNSUPPORTED, PDA_ERR_LAUNCH, PDA_ERR_WORKSPACE = range(5)
+(PDA_OK, PDA_ERR_INVALID_ARG, PDA_ERR_UNSUPPORTED, PDA_ERR_LAUNCH, PDA_ERR_WORKSPACE,
+ PDA_ERR_POOL_EXHAUSTED) = range(6)
 KV_BF16, KV_FP8_E4M3 = 0, 1
 SCALE_NONE, SCALE_PER_HEAD, SCALE_PER_TOKEN = 0, 1, 2
 
 EXPORTS = ("kv_write_fp8", "kv_write_bf16", "kv_transcode_bf16_to_fp8", "validate_page_tags",
            "paged_decode_attn_workspace_bytes", "paged_decode_attn",
-           "pda_status_string")
+           "pda_status_string", "pda_pool_create", "pda_pool_destroy", "pda_pool_alloc",
+           "pda_pool_free", "pda_pool_tags", "pda_pool_num_free")
 
 
 class PdaError(RuntimeError):
@@ -75,6 +77,18 @@ def load(path: str | None = None):
     lib.paged_decode_attn.restype = ctypes.c_int
     lib.pda_status_string.argtypes = [ctypes.c_int]
     lib.pda_status_string.restype = ctypes.c_char_p
+    lib.pda_pool_create.argtypes = [I32, V, ctypes.c_uint32, I32, ctypes.POINTER(ctypes.c_void_p)]
+    lib.pda_pool_create.restype = ctypes.c_int
+    lib.pda_pool_destroy.argtypes = [V]
+    lib.pda_pool_destroy.restype = None
+    lib.pda_pool_alloc.argtypes = [V, I32, V, V]
+    lib.pda_pool_alloc.restype = ctypes.c_int
+    lib.pda_pool_free.argtypes = [V, V, I32]
+    lib.pda_pool_free.restype = ctypes.c_int
+    lib.pda_pool_tags.argtypes = [V]
+    lib.pda_pool_tags.restype = ctypes.POINTER(ctypes.c_uint32)
+    lib.pda_pool_num_free.argtypes = [V]
+    lib.pda_pool_num_free.restype = I32
     _lib = lib
     return lib
 
@@ -195,3 +209,59 @@ def paged_decode_attn(shape: AttnShape, q, k_cache, v_cache, k_scale, v_scale, b
         workspace.numel() * workspace.element_size(), _ptr(out, elem=4, name="out"),
         _stream(stream))
     _check("paged_decode_attn", st)
+
+
+class PagePool:
+    """The host page pool and tag tracker of libpda.so (pda_pool_*), over
+    numpy arrays. alloc raises PdaError(PDA_ERR_POOL_EXHAUSTED) when fewer
+    pages are free than asked for; free raises on ids out of range, not in
+    use or repeated; in both cases nothing changes."""
+
+    def __init__(self, num_pages: int, initial_order=None, tag_start: int = 0,
+                 track_tags: bool = True):
+        import numpy as np
+        self._np = np
+        lib = load()
+        order = None
+        if initial_order is not None:
+            order = np.ascontiguousarray(initial_order, dtype=np.int32)
+            if order.size != num_pages:
+                raise ValueError("initial_order must hold num_pages ids")
+        h = ctypes.c_void_p()
+        st = lib.pda_pool_create(num_pages, None if order is None else order.ctypes.data,
+                                 tag_start & 0xFFFFFFFF, 1 if track_tags else 0,
+                                 ctypes.byref(h))
+        _check("pda_pool_create", st)
+        self._h = h
+        self.num_pages = num_pages
+
+    def close(self):
+        if getattr(self, "_h", None):
+            load().pda_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    @property
+    def num_free(self) -> int:
+        return int(load().pda_pool_num_free(self._h))
+
+    def alloc(self, n: int):
+        np = self._np
+        pages = np.empty(n, np.int32)
+        tags = np.empty(n, np.uint32)
+        st = load().pda_pool_alloc(self._h, n, pages.ctypes.data, tags.ctypes.data)
+        _check("pda_pool_alloc", st)
+        return pages, tags
+
+    def free(self, pages) -> None:
+        np = self._np
+        p = np.ascontiguousarray(pages, dtype=np.int32)
+        _check("pda_pool_free", load().pda_pool_free(self._h, p.ctypes.data, p.size))
+
+    def tags(self):
+        """Copy of the current per-page tags (uint32 [num_pages])."""
+        np = self._np
+        ptr = load().pda_pool_tags(self._h)
+        return np.ctypeslib.as_array(ptr, shape=(self.num_pages,)).copy()

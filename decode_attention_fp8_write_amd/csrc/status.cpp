@@ -8,6 +8,7 @@ extern "C" const char* pda_status_string(int status) {
     case PDA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case PDA_ERR_LAUNCH: return "kernel launch failed";
     case PDA_ERR_WORKSPACE: return "workspace too small";
+    case PDA_ERR_POOL_EXHAUSTED: return "page pool exhausted";
     default: return "unknown status";
   }
 }

@@ -71,7 +71,8 @@ enum pda_status {
   PDA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad ratio   */
   PDA_ERR_UNSUPPORTED = 2, /* valid but not built: (dtype, dims, page size) */
   PDA_ERR_LAUNCH = 3,      /* the HIP runtime rejected a kernel launch      */
-  PDA_ERR_WORKSPACE = 4    /* workspace smaller than the minimum           */
+  PDA_ERR_WORKSPACE = 4,   /* workspace smaller than the minimum           */
+  PDA_ERR_POOL_EXHAUSTED = 5 /* fewer free pages than an allocation asks for */
 };
 
 enum pda_kv_dtype { PDA_KV_BF16 = 0, PDA_KV_FP8_E4M3 = 1 };
@@ -290,6 +291,47 @@ int paged_decode_attn(const pda_attn_shape* shape, const void* q,
 
 /* Human-readable name of a status code (static storage). */
 const char* pda_status_string(int status);
+
+/*
+ * Host page pool and tag tracker — the host side of the tag check. The
+ * pages say every physical page carries a tag that changes when the page is
+ * handed out again, that each request records the pages and tags it
+ * expects, and that a no-op tracker costs nothing when the check is off
+ * ([VN] § "Bảo vệ bộ nhớ đệm dùng chung"; [DE] § "Sicherheit gemeinsamer
+ * KV-Caches wird zum Produktionsthema"; [JA] § "KV キャッシュ整合性チェック").
+ * Host memory only; no GPU call is made. A pool is not thread-safe: calls
+ * on one pool must not overlap.
+ *
+ * pda_pool_create  num_pages > 0 pages, all free. initial_order: NULL hands
+ *                  pages out as 0, 1, 2, ...; else a permutation of
+ *                  [0, num_pages) giving the order of the first hand-outs
+ *                  (rejected if it is not one). tag_start: the counter's
+ *                  start value. track_tags == 0 makes the no-op tracker: no
+ *                  tag is ever stamped (tags stay 0) and the caller passes
+ *                  verdict NULL to paged_decode_attn. *out receives the pool.
+ * pda_pool_alloc   hands out n pages, the most recently freed first
+ *                  (free pages form a stack); with tracking each hand-out
+ *                  stamps the page with ++counter (32-bit, wrapping), so a
+ *                  page handed out again carries a new tag. pages[n] and
+ *                  tags[n] receive the page ids and their new tags (tags may
+ *                  be NULL). PDA_ERR_POOL_EXHAUSTED, with nothing handed
+ *                  out, if fewer than n pages are free.
+ * pda_pool_free    returns n pages, pushed in array order (so the last one
+ *                  is handed out first). PDA_ERR_INVALID_ARG, with nothing
+ *                  freed, if an id is out of range, not in use, or repeated.
+ * pda_pool_tags    the current tag of every page, [num_pages] uint32 (valid
+ *                  until the next call on the pool); the array to upload as
+ *                  validate_page_tags' page_tags.
+ * pda_pool_num_free  free page count (-1 for a NULL pool).
+ */
+typedef struct pda_page_pool pda_page_pool;
+int pda_pool_create(int32_t num_pages, const int32_t* initial_order, uint32_t tag_start,
+                    int32_t track_tags, pda_page_pool** out);
+void pda_pool_destroy(pda_page_pool* pool);
+int pda_pool_alloc(pda_page_pool* pool, int32_t n, int32_t* pages, uint32_t* tags);
+int pda_pool_free(pda_page_pool* pool, const int32_t* pages, int32_t n);
+const uint32_t* pda_pool_tags(const pda_page_pool* pool);
+int32_t pda_pool_num_free(const pda_page_pool* pool);
 
 #ifdef __cplusplus
 }

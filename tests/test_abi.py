@@ -29,6 +29,8 @@ def pda():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     assert names == sorted(["kv_write_fp8", "kv_write_bf16", "kv_transcode_bf16_to_fp8",
+                            "pda_pool_create", "pda_pool_destroy", "pda_pool_alloc",
+                            "pda_pool_free", "pda_pool_tags", "pda_pool_num_free",
                             "validate_page_tags",
                             "paged_decode_attn_workspace_bytes", "paged_decode_attn",
                             "pda_status_string"])
