@@ -133,31 +133,27 @@ def time_plain_steps(db, steps, warmup, torch, use_verdict):
     return a.elapsed_time(b) / steps
 
 
+def pool_cycles(pool, seconds):
+    """Pages per second of alloc + free of the 512 pages of one 8192-token
+    sequence (page 16) per cycle."""
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        pages = pool.alloc(512)[0]
+        pool.free(pages)
+        n += 512
+    return n / (time.perf_counter() - t0)
+
+
 def time_page_pool(pda, np, seconds=0.3):
-    """Host page pool throughput: hand out and return the 512 pages of one
-    8192-token sequence (page 16) per cycle, tracking on and off, on a
-    32768-page pool (the 64 x 8192 workload's pool); plus the oracle's pool
-    (pure Python) for scale. Pages per second of alloc + free."""
-    from oracle.pool import OraclePagePool
-
-    def run(pool, alloc, free):
-        n, t0 = 0, time.perf_counter()
-        while time.perf_counter() - t0 < seconds:
-            pages = alloc(pool)
-            free(pool, pages)
-            n += 512
-        return n / (time.perf_counter() - t0)
-
+    """Host page pool throughput (libpda.so's pda_pool_*), tracking on and
+    off, on a 32768-page pool (the 64 x 8192 workload's pool)."""
     P = 32768
     order = np.random.default_rng(1).permutation(P)
     res = {}
     for name, track in (("tags", True), ("no_op", False)):
         pool = pda.PagePool(P, initial_order=order, track_tags=track)
-        res[f"native_{name}_pages_per_s"] = run(pool, lambda q: q.alloc(512)[0],
-                                                lambda q, p: q.free(p))
+        res[f"native_{name}_pages_per_s"] = pool_cycles(pool, seconds)
         pool.close()
-    ref = OraclePagePool(P, initial_order=order)
-    res["oracle_pages_per_s"] = run(ref, lambda q: q.alloc(512)[0], lambda q, p: q.free(p))
     return res
 
 
@@ -243,8 +239,11 @@ def cpu_baseline(batch, data, host_scales, target_s=12.0):
     t = sum(run(seqs, sub) for _ in range(reps))
     n = len(seqs) * reps
     kvb = n * int(batch.seq_lens[0]) * cfg.num_kv_heads * (cfg.head_dim_qk + cfg.head_dim_v)
+    from oracle.pool import OraclePagePool
+    pool_rate = pool_cycles(OraclePagePool(32768, initial_order=np.random.default_rng(1)
+                                           .permutation(32768)), 0.3)
     return {"value": kvb / t / 1e9, "unit": "GB/s", "cores": nthreads, "kind": "oracle",
-            "seq_steps_per_s": n / t,
+            "seq_steps_per_s": n / t, "page_pool_pages_per_s": pool_rate,
             "sample": f"{len(seqs)} whole sequences of the 64 x 8192 workload (all 64 query "
                       f"heads), {reps} steps: kv write of the newest token, tag check, fp64 "
                       f"attention; {t:.1f} s"}
