@@ -236,9 +236,10 @@ class PagePool:
         self.num_pages = num_pages
 
     def close(self):
-        if getattr(self, "_h", None):
-            load().pda_pool_destroy(self._h)
-            self._h = None
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:   # the library may be gone at interpreter exit
+            _lib.pda_pool_destroy(h)
+        self._h = None
 
     def __del__(self):
         self.close()
