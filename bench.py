@@ -157,6 +157,31 @@ def time_page_pool(pda, np, seconds=0.3):
     return res
 
 
+def read_ceiling(torch, pda, reps=10):
+    """Measured HBM read ceilings (pda_hbm_read_probe over a 4 GiB buffer):
+    one streaming pass, and 2 KB chunks in scrambled order (the per-page,
+    per-kv-head granule of the FP8 cache at page 16)."""
+    buf = torch.ones(1 << 30, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(pda.hbm_read_probe_sink_words(), dtype=torch.int32, device="cuda")
+    out = {}
+    for name, chunk in (("streaming_GBps", 0), ("random_2KB_GBps", 2048)):
+        for _ in range(2):
+            pda.hbm_read_probe(buf, chunk, sink)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            pda.hbm_read_probe(buf, chunk, sink)
+        b.record()
+        torch.cuda.synchronize()
+        out[name] = (4 << 30) / (a.elapsed_time(b) / reps * 1e-3) / 1e9
+    del buf, sink
+    torch.cuda.empty_cache()
+    log(f"measured read ceilings: {out}")
+    return out
+
+
 def time_transcode(bf, fp8, args, torch, np, pda, reps=50):
     """kv_transcode_bf16_to_fp8 of every page of the BF16 pool into a fresh
     FP8 pool of the same size through a seeded permutation, timed with HIP
@@ -392,6 +417,7 @@ def main():
     r8 = time_steps(fp8, args.steps, args.warmup, torch)
     kv8 = workload.kv_bytes(batch, pda.KV_FP8_E4M3)
     B = batch.B
+    ceiling = read_ceiling(torch, pda)
     # tag-check overhead: the same steps with the no-op tracker, interleaved
     # on/off passes so clock drift cancels
     log("timing steps with and without the tag check")
@@ -457,6 +483,7 @@ def main():
         "validate_frac_of_step": r8["validate_ms"] / r8["step_ms_with_call_events"],
         "tag_check": tracker,
         "page_pool": time_page_pool(pda, np),
+        "hbm_read_ceiling": ceiling,
         "step_ms_with_call_events": r8["step_ms_with_call_events"],
         "kv_GBps_attn": kv8 / attn_s / 1e9,
         "wall_ms_per_step": r8["wall_ms_per_step"],
@@ -464,6 +491,8 @@ def main():
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "algorithmic_bytes_per_launch": attn_bytes,
+                     "frac_of_measured_random_2KB_ceiling":
+                         achieved / ceiling["random_2KB_GBps"],
                      "traffic": measured_traffic()},
     }
     if res_bf16 is not None:

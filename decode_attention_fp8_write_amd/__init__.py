@@ -26,7 +26,8 @@ SCALE_NONE, SCALE_PER_HEAD, SCALE_PER_TOKEN = 0, 1, 2
 EXPORTS = ("kv_write_fp8", "kv_write_bf16", "kv_transcode_bf16_to_fp8", "validate_page_tags",
            "paged_decode_attn_workspace_bytes", "paged_decode_attn",
            "pda_status_string", "pda_pool_create", "pda_pool_destroy", "pda_pool_alloc",
-           "pda_pool_free", "pda_pool_tags", "pda_pool_num_free")
+           "pda_pool_free", "pda_pool_tags", "pda_pool_num_free",
+           "pda_hbm_read_probe", "pda_hbm_read_probe_sink_words")
 
 
 class PdaError(RuntimeError):
@@ -89,6 +90,10 @@ def load(path: str | None = None):
     lib.pda_pool_tags.restype = ctypes.POINTER(ctypes.c_uint32)
     lib.pda_pool_num_free.argtypes = [V]
     lib.pda_pool_num_free.restype = I32
+    lib.pda_hbm_read_probe_sink_words.argtypes = []
+    lib.pda_hbm_read_probe_sink_words.restype = ctypes.c_size_t
+    lib.pda_hbm_read_probe.argtypes = [V, ctypes.c_size_t, I32, V, V]
+    lib.pda_hbm_read_probe.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -266,3 +271,19 @@ class PagePool:
         np = self._np
         ptr = load().pda_pool_tags(self._h)
         return np.ctypeslib.as_array(ptr, shape=(self.num_pages,)).copy()
+
+
+def hbm_read_probe(buf, chunk_bytes: int, sink, stream=None):
+    """Read every byte of the CUDA tensor `buf` once (include/pda_probe.h):
+    chunk_bytes 0 streams, else scrambled chunks of that size. sink: int32
+    tensor of at least hbm_read_probe_sink_words() elements."""
+    if sink.numel() < load().pda_hbm_read_probe_sink_words():
+        raise ValueError("sink too small")
+    nbytes = buf.numel() * buf.element_size()
+    _check("pda_hbm_read_probe", load().pda_hbm_read_probe(
+        _ptr(buf, name="buf"), nbytes, chunk_bytes, _ptr(sink, elem=4, name="sink"),
+        _stream(stream)))
+
+
+def hbm_read_probe_sink_words() -> int:
+    return int(load().pda_hbm_read_probe_sink_words())

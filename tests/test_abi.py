@@ -8,11 +8,12 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pda.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([A-Za-z_]\w*)\s*\(",
                        text, flags=re.M)
@@ -31,6 +32,7 @@ def test_header_declares_the_entry_points():
     assert names == sorted(["kv_write_fp8", "kv_write_bf16", "kv_transcode_bf16_to_fp8",
                             "pda_pool_create", "pda_pool_destroy", "pda_pool_alloc",
                             "pda_pool_free", "pda_pool_tags", "pda_pool_num_free",
+                            "pda_hbm_read_probe", "pda_hbm_read_probe_sink_words",
                             "validate_page_tags",
                             "paged_decode_attn_workspace_bytes", "paged_decode_attn",
                             "pda_status_string"])
@@ -159,3 +161,17 @@ def test_transcode_argument_checks(pda):
         pda.PDA_ERR_UNSUPPORTED                             # per-token needs a latent cache
     assert call(k_src=ctypes.c_void_p(264)) == pda.PDA_ERR_INVALID_ARG   # misaligned
     assert call(Ps=0) == pda.PDA_ERR_INVALID_ARG
+
+
+def test_read_probe_argument_checks(pda):
+    lib = pda.load()
+    fake = ctypes.c_void_p(256)
+    null = None
+    E = pda.PDA_ERR_INVALID_ARG
+    assert lib.pda_hbm_read_probe(null, 4096, 0, fake, null) == E
+    assert lib.pda_hbm_read_probe(fake, 4096, 0, null, null) == E
+    assert lib.pda_hbm_read_probe(ctypes.c_void_p(264), 4096, 0, fake, null) == E   # misaligned
+    assert lib.pda_hbm_read_probe(fake, 4100, 0, fake, null) == E      # not whole 16-byte words
+    assert lib.pda_hbm_read_probe(fake, 8192, 3000, fake, null) == E   # chunk not a power of two
+    assert lib.pda_hbm_read_probe(fake, 8192, 128, fake, null) == E    # chunk too small
+    assert lib.pda_hbm_read_probe(fake, 3 * 2048, 2048, fake, null) == E   # 3 chunks
