@@ -173,8 +173,9 @@ int kv_write_bf16(const void* k_new, const void* v_new,
  *               and written to token_scale[dst_page*page_size + slot].
  *  k_dst, v_dst FP8 caches with dst_num_pages pages. Slots at or past
  *               valid[i], and pages no pair names, are left unchanged.
- *  Errors as kv_write_fp8 (page_size must also divide into whole 16-dim
- *  column groups: Dk % 16 == 0; even page_size; Dv % 8 == 0 unless latent).
+ *  Errors as kv_write_fp8: PDA_ERR_UNSUPPORTED unless Dk % 16 == 0, the
+ *  page size is even and Dv % 8 == 0 (non-latent); PER_TOKEN also needs a
+ *  page size dividing 256. Caches must be 16-byte aligned (v_dst 8).
  */
 int kv_transcode_bf16_to_fp8(const void* k_src, const void* v_src,
                              const int32_t* src_pages, const int32_t* dst_pages,
