@@ -21,24 +21,31 @@ namespace {
 constexpr int kThreads = 256;
 
 // e4m3 codes of four fp32 quotients packed little-endian into a dword, via
-// the gfx950 converter (OCP e4m3, round to nearest even). The converter is
-// fed values clamped to ±448 so it never sees an out-of-range magnitude:
-// every |y| >= 448 must give ±448, and clamping first is exact. NaN inputs get
-// the canonical NaN code with the input's sign.
+// the gfx950 converter (OCP e4m3, round to nearest even). Measured on every
+// bf16 value: the converter's codes are exact for every finite |y| below
+// 464 (values from 448 up round to 448 there) and never 0x7F/0xFF; from 464
+// up and for ±inf it returns the NaN code with the input's sign, and for a
+// NaN input 0xFF whatever its sign. So the bytes equal to 0x7F or 0xFF are
+// exactly the ones to fix: saturation (0x7E|sign) or NaN (0x7F|sign). They
+// are found four at a time with byte arithmetic; the per-element fix runs
+// only when one is present (never for data scaled into ±448).
 __device__ __forceinline__ uint32_t e4m3x4(float y0, float y1, float y2, float y3) {
-  float c0 = fminf(fmaxf(y0, -448.0f), 448.0f);
-  float c1 = fminf(fmaxf(y1, -448.0f), 448.0f);
-  float c2 = fminf(fmaxf(y2, -448.0f), 448.0f);
-  float c3 = fminf(fmaxf(y3, -448.0f), 448.0f);
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c2, c3, w, true);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, w, true);
   uint32_t r = (uint32_t)w;
-  float ys[4] = {y0, y1, y2, y3};
+  // z byte == 0 exactly where the code is 0x7F or 0xFF; every z byte is at
+  // most 0x7F, so z + 0x7F per byte never carries into the next byte
+  const uint32_t z = (r & 0x7F7F7F7Fu) ^ 0x7F7F7F7Fu;
+  const uint32_t hit = ~((z + 0x7F7F7F7Fu) | z) & 0x80808080u;
+  if (hit != 0) {
+    const float ys[4] = {y0, y1, y2, y3};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (__builtin_isnan(ys[i])) {
-      uint32_t code = 0x7Fu | ((as_u32(ys[i]) >> 31) << 7);
-      r = (r & ~(0xFFu << (8 * i))) | (code << (8 * i));
+    for (int i = 0; i < 4; ++i) {
+      if (hit & (0x80u << (8 * i))) {
+        const uint32_t sgn = (as_u32(ys[i]) >> 31) << 7;
+        const uint32_t code = (__builtin_isnan(ys[i]) ? 0x7Fu : 0x7Eu) | sgn;
+        r = (r & ~(0xFFu << (8 * i))) | (code << (8 * i));
+      }
     }
   }
   return r;
