@@ -28,8 +28,12 @@ constexpr int kThreads = 256;
 // NaN input 0xFF whatever its sign. So the bytes equal to 0x7F or 0xFF are
 // exactly the ones to fix: saturation (0x7E|sign) or NaN (0x7F|sign). They
 // are found four at a time with byte arithmetic; the per-element fix runs
-// only when one is present (never for data scaled into ±448).
-__device__ __forceinline__ uint32_t e4m3x4(float y0, float y1, float y2, float y3) {
+// only when one is present (never for data scaled into ±448). The fix takes
+// NaN-ness and sign from f: the quotient itself, or the dividend where the
+// quotient of a positive finite scale was computed in a way that can turn
+// an infinite dividend into NaN.
+__device__ __forceinline__ uint32_t e4m3x4(float y0, float y1, float y2, float y3, float f0,
+                                           float f1, float f2, float f3) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, w, true);
   uint32_t r = (uint32_t)w;
@@ -38,17 +42,21 @@ __device__ __forceinline__ uint32_t e4m3x4(float y0, float y1, float y2, float y
   const uint32_t z = (r & 0x7F7F7F7Fu) ^ 0x7F7F7F7Fu;
   const uint32_t hit = ~((z + 0x7F7F7F7Fu) | z) & 0x80808080u;
   if (hit != 0) {
-    const float ys[4] = {y0, y1, y2, y3};
+    const float fs[4] = {f0, f1, f2, f3};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (hit & (0x80u << (8 * i))) {
-        const uint32_t sgn = (as_u32(ys[i]) >> 31) << 7;
-        const uint32_t code = (__builtin_isnan(ys[i]) ? 0x7Fu : 0x7Eu) | sgn;
+        const uint32_t sgn = (as_u32(fs[i]) >> 31) << 7;
+        const uint32_t code = (__builtin_isnan(fs[i]) ? 0x7Fu : 0x7Eu) | sgn;
         r = (r & ~(0xFFu << (8 * i))) | (code << (8 * i));
       }
     }
   }
   return r;
+}
+
+__device__ __forceinline__ uint32_t e4m3x4(float y0, float y1, float y2, float y3) {
+  return e4m3x4(y0, y1, y2, y3, y0, y1, y2, y3);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return as_f32(w << 16); }
@@ -173,6 +181,33 @@ __device__ __forceinline__ uint2 encode8(uint4 x, float sc) {
                            bf16_hi(x.w) / sc));
 }
 
+// Division by a scale through its reciprocal. With y = 1/s correctly
+// rounded, q0 = x*y, the residual r = q0*s - x (exact in one fma) and
+// q = q0 - r*y rounded once, q is the correctly rounded quotient x / s (the
+// reciprocal-based correction step of Markstein's division) as long as the
+// residual cannot underflow. For bf16 x and s in [2^-64, 2^64] that holds
+// for every quotient of magnitude 2^-11 or more; smaller quotients come out
+// below 2^-10 with the right sign, which encodes to the same ±0 code. The
+// residual's sign is taken so that x = -0 gives -0. Compared on the host with
+// the correctly rounded division over all bf16 x for 10^5 scales spread over
+// that interval and beyond it: identical inside, wrong near 2^-92 and below.
+__device__ __forceinline__ bool fast_divisor(float s) { return s >= 0x1p-64f && s <= 0x1p64f; }
+
+__device__ __forceinline__ float quot(float x, float s, float y) {
+  const float q0 = x * y;
+  const float r = __builtin_fmaf(q0, s, -x);
+  return __builtin_fmaf(-r, y, q0);
+}
+
+__device__ __forceinline__ uint32_t encode4_rcp(uint32_t a, uint32_t b, float s, float y) {
+  const float x0 = bf16_lo(a), x1 = bf16_hi(a), x2 = bf16_lo(b), x3 = bf16_hi(b);
+  return e4m3x4(quot(x0, s, y), quot(x1, s, y), quot(x2, s, y), quot(x3, s, y), x0, x1, x2, x3);
+}
+
+__device__ __forceinline__ uint2 encode8_rcp(uint4 x, float s, float y) {
+  return make_uint2(encode4_rcp(x.x, x.y, s, y), encode4_rcp(x.z, x.w, s, y));
+}
+
 __device__ __forceinline__ bool pair_ok(int src, int dst, int n, int ps, int pd, int S) {
   return src >= 0 && src < ps && dst >= 0 && dst < pd && n >= 0 && n <= S;
 }
@@ -181,11 +216,12 @@ __device__ __forceinline__ bool pair_ok(int src, int dst, int n, int ps, int pd,
 // are contiguous (Hkv*S*Dk K elements, then Hkv*S*Dv V elements), each
 // thread takes 8 elements per step, four steps' loads issued before their
 // conversions and stores.
-template <bool V>
+template <bool V, bool FAST>
 __device__ __forceinline__ void transcode_span(const uint16_t* __restrict__ src,
                                                uint8_t* __restrict__ dst, int n_elems,
                                                int head_elems, int S, int D, int valid,
-                                               const float* __restrict__ scale) {
+                                               const float* __restrict__ scale,
+                                               const float* __restrict__ rcp) {
   constexpr int U = 4;
   for (int e0 = threadIdx.x * 8; e0 < n_elems; e0 += kThreads * 8 * U) {
     uint4 x[U];
@@ -202,7 +238,7 @@ __device__ __forceinline__ void transcode_span(const uint16_t* __restrict__ src,
       const int eh = e - h * head_elems;
       const int s0 = V ? v_slot(eh, D) : k_slot(eh, S);
       if (s0 >= valid) continue;
-      const uint2 c = encode8(x[u], scale[h]);
+      const uint2 c = FAST ? encode8_rcp(x[u], scale[h], rcp[h]) : encode8(x[u], scale[h]);
       if (!V || s0 + 1 < valid) {
         *reinterpret_cast<uint2*>(dst + e) = c;
       } else {   // only the even slot of a V pair: its four bytes
@@ -216,22 +252,52 @@ __device__ __forceinline__ void transcode_span(const uint16_t* __restrict__ src,
   }
 }
 
+// Reciprocals of the K and V scales of up to kMaxRcpHeads kv heads are
+// kept in LDS; with more heads, or any scale outside the fast divisor
+// interval, the workgroup divides instead.
+constexpr int kMaxRcpHeads = 256;
+
 __global__ __launch_bounds__(kThreads) void kv_transcode_head_kernel(
     const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src,
     const int32_t* __restrict__ src_pages, const int32_t* __restrict__ dst_pages,
     const int32_t* __restrict__ valid, int hkv, int dk, int dv, int S, int ps, int pd,
     const float* __restrict__ k_scale, const float* __restrict__ v_scale,
     uint8_t* __restrict__ k_dst, uint8_t* __restrict__ v_dst) {
+  __shared__ float rcp[2 * kMaxRcpHeads];
+  __shared__ int slow;
   const int pair = blockIdx.x;
   const int src = src_pages[pair], dst = dst_pages[pair], n = valid[pair];
   if (!pair_ok(src, dst, n, ps, pd, S) || n == 0) return;
+  const int nsc = (v_src == nullptr) ? hkv : 2 * hkv;
+  bool fast = hkv <= kMaxRcpHeads;
+  if (fast) {
+    if (threadIdx.x == 0) slow = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < nsc; i += kThreads) {
+      const float sc = (i < hkv) ? k_scale[i] : v_scale[i - hkv];
+      if (fast_divisor(sc))
+        rcp[i] = 1.0f / sc;
+      else
+        slow = 1;
+    }
+    __syncthreads();
+    fast = (slow == 0);
+  }
   const int nk = hkv * S * dk;
-  transcode_span<false>(k_src + (int64_t)src * nk, k_dst + (int64_t)dst * nk, nk, S * dk, S,
-                        dk, n, k_scale);
+  const uint16_t* ks = k_src + (int64_t)src * nk;
+  uint8_t* kd = k_dst + (int64_t)dst * nk;
+  if (fast)
+    transcode_span<false, true>(ks, kd, nk, S * dk, S, dk, n, k_scale, rcp);
+  else
+    transcode_span<false, false>(ks, kd, nk, S * dk, S, dk, n, k_scale, rcp);
   if (v_src == nullptr) return;
   const int nv = hkv * S * dv;
-  transcode_span<true>(v_src + (int64_t)src * nv, v_dst + (int64_t)dst * nv, nv, S * dv, S, dv,
-                       n, v_scale);
+  const uint16_t* vs = v_src + (int64_t)src * nv;
+  uint8_t* vd = v_dst + (int64_t)dst * nv;
+  if (fast)
+    transcode_span<true, true>(vs, vd, nv, S * dv, S, dv, n, v_scale, rcp + hkv);
+  else
+    transcode_span<true, false>(vs, vd, nv, S * dv, S, dv, n, v_scale, rcp + hkv);
 }
 
 // One workgroup per pair, latent cache (Hkv == 1, K only), per-token scales:
@@ -270,12 +336,23 @@ __global__ __launch_bounds__(kThreads) void kv_transcode_token_kernel(
       for (int i = 0; i < per; ++i) m = fmaxf(m, red[i * (kThreads / per) + threadIdx.x % (kThreads / per)]);
       const float sc = (m > 0.0f) ? m / 448.0f : 1.0f;
       if (q == 0) token_scale[(int64_t)dst * S + t] = sc;
-      for (int c = q; c < groups; c += per) {
-        const int64_t o = ((int64_t)c * S + t) * 16;
-        const uint4 a = *reinterpret_cast<const uint4*>(k_src + sb + o);
-        const uint4 b = *reinterpret_cast<const uint4*>(k_src + sb + o + 8);
-        const uint2 ca = encode8(a, sc), cb = encode8(b, sc);
-        *reinterpret_cast<uint4*>(k_dst + db + o) = make_uint4(ca.x, ca.y, cb.x, cb.y);
+      if (fast_divisor(sc)) {
+        const float y = 1.0f / sc;
+        for (int c = q; c < groups; c += per) {
+          const int64_t o = ((int64_t)c * S + t) * 16;
+          const uint4 a = *reinterpret_cast<const uint4*>(k_src + sb + o);
+          const uint4 b = *reinterpret_cast<const uint4*>(k_src + sb + o + 8);
+          const uint2 ca = encode8_rcp(a, sc, y), cb = encode8_rcp(b, sc, y);
+          *reinterpret_cast<uint4*>(k_dst + db + o) = make_uint4(ca.x, ca.y, cb.x, cb.y);
+        }
+      } else {
+        for (int c = q; c < groups; c += per) {
+          const int64_t o = ((int64_t)c * S + t) * 16;
+          const uint4 a = *reinterpret_cast<const uint4*>(k_src + sb + o);
+          const uint4 b = *reinterpret_cast<const uint4*>(k_src + sb + o + 8);
+          const uint2 ca = encode8(a, sc), cb = encode8(b, sc);
+          *reinterpret_cast<uint4*>(k_dst + db + o) = make_uint4(ca.x, ca.y, cb.x, cb.y);
+        }
       }
     }
     __syncthreads();   // red is reused by the next round of slots

@@ -144,3 +144,116 @@ def test_transcode_full_pool_sampled(gpu):
     gv = vd.view(P, nv)[torch.from_numpy(dst[sample].astype(np.int64)).cuda()].cpu().numpy()
     assert np.array_equal(gk.ravel(), okd), "K pages differ"
     assert np.array_equal(gv.ravel(), ovd), "V pages differ"
+
+
+def _pattern_pages(P, hkv, S, D, shift):
+    """P pages whose (page, head) blocks hold every bf16 bit pattern in turn,
+    each head's run rotated by `shift` patterns so heads see different values."""
+    n = S * D
+    e = np.arange(P * n, dtype=np.int64) % (P * n)
+    out = np.empty(P * hkv * n, np.uint16)
+    v = out.reshape(P, hkv, n)
+    for h in range(hkv):
+        v[:, h, :] = ((e + h * shift) & 0xFFFF).reshape(P, n)
+    return out
+
+
+SCALE_SETS = {
+    # every scale inside [2^-64, 2^64]: reciprocal path
+    "fast": [1.0, 0.0123, 3.0, 2.0 ** -64, 2.0 ** 64, float(np.float32(1.9999999)),
+             7.3 / 448, 1e-5],
+    # one scale outside the interval sends the whole page through the division
+    "mixed": [1.0, 2.0 ** -70, 0.02, 0.5, 3.0, 0.0123, 1e-5, 0.25],
+    "far": [2.0 ** 70, 2.0 ** -100, 1e-38, 3e37, 2.0 ** 65, 2.0 ** -65, 1e-30, 1e30],
+}
+
+
+@pytest.mark.parametrize("name", sorted(SCALE_SETS))
+def test_transcode_all_bf16_patterns(gpu, name):
+    """Per-head scales: every bf16 pattern of K and V under each of 8 head
+    scales, bit-exact against the oracle."""
+    hkv, dk, dv, S = 8, 128, 128, 16
+    P = 65536 // (S * dk)
+    log(f"transcode all bf16 patterns, scales {name}")
+    kc = _pattern_pages(P, hkv, S, dk, 977)
+    vc = _pattern_pages(P, hkv, S, dv, 3001)
+    kscale = np.float32(SCALE_SETS[name])
+    vscale = np.float32(SCALE_SETS[name][::-1])
+    src = np.arange(P, dtype=np.int32)
+    dst = src[::-1].copy()
+    valid = np.full(P, S, np.int32)
+    valid[3] = 5
+    kd = np.full(P * hkv * S * dk, SENT, np.uint8)
+    vd = np.full(P * hkv * S * dv, SENT, np.uint8)
+    oracle.kv_transcode_bf16_to_fp8(kc, vc, src, dst, valid, hkv, dk, dv, S, P, P,
+                                    synth.SCALE_PER_HEAD, kscale, vscale, None, kd, vd)
+    gkd = torch.full((kd.size,), SENT, dtype=torch.uint8, device="cuda")
+    gvd = torch.full((vd.size,), SENT, dtype=torch.uint8, device="cuda")
+    gpu.kv_transcode_bf16_to_fp8(
+        _dev(kc), _dev(vc), _dev(src), _dev(dst), _dev(valid), gkd, gvd, num_kv_heads=hkv,
+        head_dim_k=dk, head_dim_v=dv, page_size=S, src_num_pages=P, dst_num_pages=P,
+        scale_mode=synth.SCALE_PER_HEAD, k_scale=_dev(kscale), v_scale=_dev(vscale))
+    torch.cuda.synchronize()
+    for what, g, o in (("K", gkd, kd), ("V", gvd, vd)):
+        got = g.cpu().numpy()
+        bad = np.nonzero(got != o)[0]
+        if bad.size:
+            log(f"{what} mismatches {bad.size}: idx {bad[:6].tolist()} gpu "
+                f"{got[bad[:6]].tolist()} oracle {o[bad[:6]].tolist()}")
+        assert bad.size == 0, f"{what} bytes differ"
+
+
+def test_transcode_per_token_scale_ranges(gpu):
+    """Latent pages with per-token scales inside and outside [2^-64, 2^64]:
+    rows of bf16 patterns up to 2^20 in magnitude plus NaNs (reciprocal path),
+    rows of subnormals only (subnormal scale), rows holding an infinity
+    (infinite scale), rows near the bf16 maximum, and all-zero rows (scale 1)."""
+    dk, S = 576, 64
+    rng = np.random.default_rng(31)
+    allp = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    f = synth.bf16_to_f32(allp)
+    with np.errstate(invalid="ignore"):
+        mid = allp[np.isnan(f) | (np.abs(f) <= 2.0 ** 20)]
+        sub = allp[(np.abs(f) < 2.0 ** -126) & ~np.isnan(f)]
+        big = allp[np.isfinite(f) & (np.abs(f) >= 2.0 ** 100)]
+    rows = []
+    for i in range(0, mid.size, dk):
+        r = mid[i:i + dk]
+        rows.append(np.concatenate([r, rng.choice(mid, dk - r.size)]) if r.size < dk else r)
+    for _ in range(16):
+        rows.append(rng.choice(sub, dk))
+        r = rng.choice(mid, dk)
+        r[rng.integers(0, dk)] = 0x7F80 if rng.random() < 0.5 else 0xFF80
+        rows.append(r)
+        rows.append(rng.choice(big, dk))
+        rows.append(np.zeros(dk, np.uint16))
+    rows = np.stack(rows)
+    order = rng.permutation(rows.shape[0])
+    rows = rows[order]
+    P = rows.shape[0] // S + 1
+    slots = np.zeros((P * S, dk), np.uint16)
+    slots[:rows.shape[0]] = rows
+    # latent K format: [page][column group][slot][16]
+    kc = slots.reshape(P, S, dk // 16, 16).transpose(0, 2, 1, 3).copy().ravel()
+    src = np.arange(P, dtype=np.int32)
+    dst = np.roll(src, 3)
+    valid = np.full(P, S, np.int32)
+    kd = np.full(P * S * dk, SENT, np.uint8)
+    ts = np.full(P * S, -7.0, np.float32)
+    oracle.kv_transcode_bf16_to_fp8(kc, None, src, dst, valid, 1, dk, 0, S, P, P,
+                                    synth.SCALE_PER_TOKEN, None, None, ts, kd, None)
+    log(f"per-token scale ranges: {rows.shape[0]} rows over {P} pages")
+    gkd = torch.full((kd.size,), SENT, dtype=torch.uint8, device="cuda")
+    gts = torch.full((P * S,), -7.0, dtype=torch.float32, device="cuda")
+    gpu.kv_transcode_bf16_to_fp8(
+        _dev(kc), None, _dev(src), _dev(dst), _dev(valid), gkd, None, num_kv_heads=1,
+        head_dim_k=dk, head_dim_v=0, page_size=S, src_num_pages=P, dst_num_pages=P,
+        scale_mode=synth.SCALE_PER_TOKEN, k_scale=None, v_scale=None, token_scale=gts)
+    torch.cuda.synchronize()
+    assert np.array_equal(gts.cpu().numpy().view(np.uint32), ts.view(np.uint32))
+    got = gkd.cpu().numpy()
+    bad = np.nonzero(got != kd)[0]
+    if bad.size:
+        log(f"K mismatches {bad.size}: idx {bad[:6].tolist()} gpu {got[bad[:6]].tolist()} "
+            f"oracle {kd[bad[:6]].tolist()}")
+    assert bad.size == 0, "K bytes differ"
