@@ -67,6 +67,8 @@ def _load():
         i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, f64,
         P, P, P, P, P, P, P, P, P, P, i32, i32]
     lib.oracle_paged_decode_attn.restype = None
+    lib.oracle_int4_gemv.argtypes = [P, P, P, i32, i32, i32, i32, P, i32, P, P]
+    lib.oracle_int4_gemv.restype = ctypes.c_int
     _ = i64
     _lib = lib
     return lib
@@ -225,3 +227,27 @@ def paged_decode_attn(q, k_cache, v_cache, k_scale, v_scale, block_table,
         _ptr(block_table), _ptr(seq_lens), _ptr(verdict), _ptr(out),
         _ptr(rows_arr), n_rows, int(num_threads))
     return out
+
+
+# --- INT4 weight-only GEMV ---------------------------------------------------
+
+def int4_gemv(x, w, scale, group=128, cols=None):
+    """y[m][n] = x @ dequant(w)^T in fp64, and sum |x * W| per output.
+    x: uint16 bf16 bits [m][k]; w: uint32 [n][k/8] (code j of a word is
+    element 8*word + j, two's complement in bits 4j..4j+3); scale: uint16
+    bf16 bits [n][k/group]. cols: optional output columns to compute (the
+    others are NaN)."""
+    x = _arr(x, np.uint16)
+    w = _arr(w, np.uint32)
+    scale = _arr(scale, np.uint16)
+    m, k = x.shape
+    n = w.shape[0]
+    assert w.shape == (n, k // 8) and scale.shape == (n, k // group)
+    y = np.full((m, n), np.nan)
+    ya = np.full((m, n), np.nan)
+    c = None if cols is None else np.ascontiguousarray(np.asarray(cols, np.int32))
+    rc = _load().oracle_int4_gemv(_ptr(x), _ptr(w), _ptr(scale), m, n, k, group, _ptr(c),
+                                  0 if c is None else c.size, _ptr(y), _ptr(ya))
+    if rc != 0:
+        raise ValueError("oracle_int4_gemv: invalid arguments")
+    return y, ya

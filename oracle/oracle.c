@@ -410,3 +410,36 @@ void oracle_paged_decode_attn(
   free(jobs);
   free(th);
 }
+
+/* ---- INT4 weight-only GEMV: the definition, one output at a time ---- */
+
+/* value of code j (0..7) of a packed word: bits 4j..4j+3 as two's complement */
+static int int4_code(uint32_t word, int j) {
+  int u = (int)((word >> (4 * j)) & 0xFu);
+  return u >= 8 ? u - 16 : u;
+}
+
+int oracle_int4_gemv(const uint16_t* x, const uint32_t* w, const uint16_t* scale,
+                     int32_t m, int32_t n, int32_t k, int32_t group,
+                     const int32_t* cols, int32_t n_cols, double* y, double* yabs) {
+  if (m < 0 || n < 0 || k < 0 || group <= 0 || k % group != 0 || k % 8 != 0) return -1;
+  int32_t count = cols ? n_cols : n;
+  for (int32_t ci = 0; ci < count; ++ci) {
+    int32_t c = cols ? cols[ci] : ci;
+    if (c < 0 || c >= n) return -1;
+    for (int32_t i = 0; i < m; ++i) {
+      double acc = 0.0, aabs = 0.0;
+      for (int32_t kk = 0; kk < k; ++kk) {
+        uint32_t word = w[(size_t)c * (k / 8) + kk / 8];
+        double wv = (double)int4_code(word, kk % 8) *
+                    (double)oracle_bf16_to_f32(scale[(size_t)c * (k / group) + kk / group]);
+        double t = (double)oracle_bf16_to_f32(x[(size_t)i * k + kk]) * wv;
+        acc += t;
+        aabs += fabs(t);
+      }
+      y[(size_t)i * n + c] = acc;
+      yabs[(size_t)i * n + c] = aabs;
+    }
+  }
+  return 0;
+}

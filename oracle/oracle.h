@@ -108,6 +108,26 @@ void oracle_paged_decode_attn(
     const int32_t* verdict, float* out, const int32_t* rows, int32_t n_rows,
     int32_t num_threads);
 
+/* --- INT4 weight-only decode GEMV ------------------------------------------
+ * The pages report INT4 weights for the decode phase, where the weights are
+ * streamed from memory for every generated token (aifeed.sk, "Cloudflare
+ * zrýchľuje inferenciu modelov Kimi a GLM kompresiou cache a váh", section
+ * "Kompresia sa oplatí inde pri vstupe a inde pri výstupe"; the German page
+ * "Cloudflare-Optimierungen für Kimi und GLM", section "GLM-
+ * Gewichtskomprimierung verschiebt den Phasen-Trade-off"). They fix no
+ * format; the reading taken here: weight W[n][kk] = q[n][kk] * scale[n][kk/G]
+ * with q a signed two's-complement 4-bit code, eight codes per uint32 word
+ * along kk (code j of word w is element kk = 8w + j, in bits 4j..4j+3),
+ * w[n][k/8]; scale bf16 [n][k/G]; x bf16 [m][k].
+ *   y[i][c]    = sum_kk x[i][kk] * W[c][kk]         (fp64, plain loop)
+ *   yabs[i][c] = sum_kk |x[i][kk] * W[c][kk]|       (for error bounds)
+ * cols: optional list of n_cols output columns to compute (NULL: all n);
+ * y and yabs are [m][n] and only the listed columns are written.
+ * Returns 0, or -1 for k not a multiple of G or of 8, G <= 0, m, n < 0. */
+int oracle_int4_gemv(const uint16_t* x, const uint32_t* w, const uint16_t* scale,
+                     int32_t m, int32_t n, int32_t k, int32_t group,
+                     const int32_t* cols, int32_t n_cols, double* y, double* yabs);
+
 #ifdef __cplusplus
 }
 #endif
