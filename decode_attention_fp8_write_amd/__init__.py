@@ -27,7 +27,7 @@ EXPORTS = ("kv_write_fp8", "kv_write_bf16", "kv_transcode_bf16_to_fp8", "validat
            "paged_decode_attn_workspace_bytes", "paged_decode_attn",
            "pda_status_string", "pda_pool_create", "pda_pool_destroy", "pda_pool_alloc",
            "pda_pool_free", "pda_pool_tags", "pda_pool_num_free",
-           "pda_hbm_read_probe", "pda_hbm_read_probe_sink_words")
+           "pda_hbm_read_probe", "pda_hbm_read_probe_sink_words", "int4_gemv_bf16")
 
 
 class PdaError(RuntimeError):
@@ -94,6 +94,8 @@ def load(path: str | None = None):
     lib.pda_hbm_read_probe_sink_words.restype = ctypes.c_size_t
     lib.pda_hbm_read_probe.argtypes = [V, ctypes.c_size_t, I32, V, V]
     lib.pda_hbm_read_probe.restype = ctypes.c_int
+    lib.int4_gemv_bf16.argtypes = [V, V, V, I32, I32, I32, I32, V, V]
+    lib.int4_gemv_bf16.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -287,3 +289,16 @@ def hbm_read_probe(buf, chunk_bytes: int, sink, stream=None):
 
 def hbm_read_probe_sink_words() -> int:
     return int(load().pda_hbm_read_probe_sink_words())
+
+
+def int4_gemv_bf16(x, w, scale, y, *, group=128, stream=None):
+    """y[m][n] = x[m][k] . dequant(w)^T (include/pda_int4.h). x: bf16 (or
+    int16 bits) [m, k]; w: int32/uint32 [n, k/8] of packed two's-complement
+    4-bit codes; scale: bf16 (or int16 bits) [n, k/group]; y: float32 [m, n]."""
+    m, k = x.shape
+    n = w.shape[0]
+    if w.shape != (n, k // 8) or scale.shape != (n, k // group) or y.shape != (m, n):
+        raise ValueError("int4_gemv_bf16: shapes do not match")
+    _check("int4_gemv_bf16", load().int4_gemv_bf16(
+        _ptr(x, elem=2, name="x"), _ptr(w, elem=4, name="w"), _ptr(scale, elem=2, name="scale"),
+        m, n, k, group, _ptr(y, elem=4, name="y"), _stream(stream)))

@@ -1,0 +1,50 @@
+/*
+ * pda_int4.h — weight-only INT4 GEMV for the decode phase, part of libpda.so.
+ *
+ * The pages report that INT4 weights (from FP8) make decode faster, since
+ * each generated token streams the weights from HBM and fewer bytes move,
+ * while prefill, compute-bound, gets slower from the unpacking; hence INT4
+ * weights for decode next to the FP8 KV cache (aifeed.sk, "Cloudflare
+ * zrýchľuje inferenciu modelov Kimi a GLM kompresiou cache a váh", section
+ * "Kompresia sa oplatí inde pri vstupe a inde pri výstupe"; the German page
+ * "Cloudflare-Optimierungen für Kimi und GLM", section "GLM-
+ * Gewichtskomprimierung verschiebt den Phasen-Trade-off"). The pages fix no
+ * format. The one taken here: signed two's-complement 4-bit codes with one
+ * scale per 128 consecutive inputs of each output row.
+ */
+#ifndef PDA_INT4_H
+#define PDA_INT4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * int4_gemv_bf16 — y[i][c] = sum_kk x[i][kk] * q[c][kk] * scale[c][kk / 128]
+ *  x      device bf16 [m][k], 16-byte aligned (activations of m tokens).
+ *  w      device uint32 [n][k / 8], 8-byte aligned: code j (bits 4j..4j+3,
+ *         two's complement, -8..7) of word kk / 8 of row c is q[c][kk] for
+ *         kk = 8 * word + j.
+ *  scale  device bf16 [n][k / 128], 2-byte aligned.
+ *  m, n, k  tokens, output rows, inputs; k a multiple of 128.
+ *  group  must be 128 (the scale group length).
+ *  y      device fp32 [m][n], 4-byte aligned; written, never read.
+ * Arithmetic: products and sums in fp32 (bf16 dot-product pairs), one fp32
+ * accumulator per output; the result differs from the exact sum by at most
+ * a few dozen fp32 roundings of sum_kk |x[i][kk]| * 144 * |scale|.
+ * Asynchronous on `stream`; nothing is allocated. Returns 0,
+ * PDA_ERR_INVALID_ARG (1) for negative sizes, NULL or misaligned pointers,
+ * PDA_ERR_UNSUPPORTED (2) for group != 128, k not a positive multiple of 128
+ * (k == 0 with m, n > 0 included) or more than 524280 tokens, PDA_ERR_LAUNCH
+ * (3) on a launch failure. m == 0 or n == 0 does nothing.
+ */
+int int4_gemv_bf16(const void* x, const uint32_t* w, const void* scale, int32_t m, int32_t n,
+                   int32_t k, int32_t group, float* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PDA_INT4_H */

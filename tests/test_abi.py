@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
                             "pda_pool_create", "pda_pool_destroy", "pda_pool_alloc",
                             "pda_pool_free", "pda_pool_tags", "pda_pool_num_free",
                             "pda_hbm_read_probe", "pda_hbm_read_probe_sink_words",
-                            "validate_page_tags",
+                            "int4_gemv_bf16", "validate_page_tags",
                             "paged_decode_attn_workspace_bytes", "paged_decode_attn",
                             "pda_status_string"])
 
@@ -175,3 +175,25 @@ def test_read_probe_argument_checks(pda):
     assert lib.pda_hbm_read_probe(fake, 8192, 3000, fake, null) == E   # chunk not a power of two
     assert lib.pda_hbm_read_probe(fake, 8192, 128, fake, null) == E    # chunk too small
     assert lib.pda_hbm_read_probe(fake, 3 * 2048, 2048, fake, null) == E   # 3 chunks
+
+
+def test_int4_gemv_argument_checks(pda):
+    lib = pda.load()
+    f = ctypes.c_void_p(4096)
+    null = None
+    E, U, OK = pda.PDA_ERR_INVALID_ARG, pda.PDA_ERR_UNSUPPORTED, pda.PDA_OK
+    g = lib.int4_gemv_bf16
+    assert g(f, f, f, -1, 16, 128, 128, f, null) == E
+    assert g(f, f, f, 1, -16, 128, 128, f, null) == E
+    assert g(f, f, f, 1, 16, 128, 64, f, null) == U          # group other than 128
+    assert g(f, f, f, 1, 16, 200, 128, f, null) == U         # k not a multiple of 128
+    assert g(f, f, f, 1, 16, 0, 128, f, null) == U           # k == 0 with work to do
+    assert g(null, null, null, 0, 16, 128, 128, null, null) == OK   # nothing to do
+    assert g(null, null, null, 4, 0, 128, 128, null, null) == OK
+    assert g(null, f, f, 1, 16, 128, 128, f, null) == E
+    assert g(f, f, f, 1, 16, 128, 128, null, null) == E
+    assert g(ctypes.c_void_p(4104), f, f, 1, 16, 128, 128, f, null) == E   # x not 16-aligned
+    assert g(f, ctypes.c_void_p(4100), f, 1, 16, 128, 128, f, null) == E   # w not 8-aligned
+    assert g(f, f, ctypes.c_void_p(4097), 1, 16, 128, 128, f, null) == E   # scale odd
+    assert g(f, f, f, 1, 16, 128, 128, ctypes.c_void_p(4098), null) == E   # y not 4-aligned
+    assert g(f, f, f, 524281, 16, 128, 128, f, null) == U    # too many tokens for the grid
