@@ -224,6 +224,88 @@ def time_transcode(bf, fp8, args, torch, np, pda, reps=50):
                          "frac": gbps / HBM_PEAK_GBPS}}
 
 
+def time_int4(torch, pda, n=8192, k=8192, batches=(1, 8, 16, 32, 64), nmat=16, reps=64):
+    """int4_gemv_bf16 on an n x k weight matrix, cycling through `nmat`
+    independent matrices (more bytes than the chip's caches hold, so every
+    call streams its weights from HBM), timed with HIP events on the launch
+    stream; beside it the same product with dense bf16 weights through
+    torch's linear (hipBLASLt), the format the INT4 weights replace.
+    Algorithmic bytes per call: codes n*k/2, scales n*k/128*2, x m*k*2,
+    y m*n*4."""
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    ws = [torch.randint(-2 ** 31, 2 ** 31 - 1, (n, k // 8), generator=gen, dtype=torch.int32,
+                        device="cuda") for _ in range(nmat)]
+    ss = [((torch.rand((n, k // 128), generator=gen, device="cuda") - 0.5) * 0.1)
+          .to(torch.bfloat16) for _ in range(nmat)]
+    out = {"shape": {"n": n, "k": k}, "matrices_cycled": nmat, "by_tokens": {}}
+    for m in batches:
+        x = torch.randn((m, k), generator=gen, device="cuda").to(torch.bfloat16)
+        y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+
+        def call(i):
+            pda.int4_gemv_bf16(x, ws[i % nmat], ss[i % nmat], y)
+
+        for i in range(8):
+            call(i)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            call(i)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        nbytes = n * k // 2 + n * (k // 128) * 2 + m * k * 2 + m * n * 4
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out["by_tokens"][str(m)] = {
+            "us": ms * 1e3, "algorithmic_bytes": nbytes, "GBps": gbps,
+            "frac_hbm": gbps / HBM_PEAK_GBPS, "TFLOPs": 2.0 * m * n * k / (ms * 1e-3) / 1e12}
+        log(f"int4 gemv m={m}: {ms * 1e3:.2f} us, {gbps:.0f} GB/s")
+    # dense bf16 weights of the same shape, same cycling
+    wb = [torch.randn((n, k), generator=gen, device="cuda").to(torch.bfloat16)
+          for _ in range(nmat)]
+    for m in batches:
+        x = torch.randn((m, k), generator=gen, device="cuda").to(torch.bfloat16)
+        for i in range(8):
+            torch.nn.functional.linear(x, wb[i % nmat])
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            torch.nn.functional.linear(x, wb[i % nmat])
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        r = out["by_tokens"][str(m)]
+        r["bf16_dense_us"] = ms * 1e3
+        r["speedup_vs_bf16_dense"] = ms * 1e3 / r["us"]
+        log(f"bf16 dense linear m={m}: {ms * 1e3:.2f} us")
+    r1 = out["by_tokens"][str(batches[0])]
+    out["roofline"] = {"kernel": "int4_gemv_kernel", "tokens": batches[0], "bound": "hbm",
+                       "achieved": r1["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                       "frac": r1["frac_hbm"]}
+    del ws, ss, wb
+    torch.cuda.empty_cache()
+    return out
+
+
+def int4_oracle_rate(np, synth, n=8192, k=8192, cols=2048):
+    """The oracle's INT4 GEMV for one token on `cols` output columns of an
+    n x k matrix, scaled to whole GEMVs per second."""
+    import oracle
+    rng = np.random.default_rng(3)
+    x = synth.bf16_from_f32(rng.standard_normal((1, k)).astype(np.float32))
+    w = rng.integers(0, 1 << 32, (n, k // 8), dtype=np.uint64).astype(np.uint32)
+    s = synth.bf16_from_f32(rng.uniform(-0.05, 0.05, (n, k // 128)).astype(np.float32))
+    t0 = time.perf_counter()
+    oracle.int4_gemv(x, w, s, cols=np.arange(cols))
+    t = time.perf_counter() - t0
+    return {"gemv_per_s": cols / n / t, "cores": 1,
+            "sample": f"{cols} of {n} output columns, 1 token, k {k}; {t:.2f} s"}
+
+
 def cpu_baseline(batch, data, host_scales, target_s=12.0):
     """The oracle (fp64, plain loops, all host threads) running the same
     step on whole sequences of the workload: kv write of the newest token,
@@ -269,6 +351,7 @@ def cpu_baseline(batch, data, host_scales, target_s=12.0):
                                            .permutation(32768)), 0.3)
     return {"value": kvb / t / 1e9, "unit": "GB/s", "cores": nthreads, "kind": "oracle",
             "seq_steps_per_s": n / t, "page_pool_pages_per_s": pool_rate,
+            "int4_gemv": int4_oracle_rate(np, synth),
             "sample": f"{len(seqs)} whole sequences of the 64 x 8192 workload (all 64 query "
                       f"heads), {reps} steps: kv write of the newest token, tag check, fp64 "
                       f"attention; {t:.1f} s"}
@@ -445,6 +528,8 @@ def main():
         res_bf16["transcode"] = time_transcode(bf, fp8, args, torch, np, pda)
         del bf
         torch.cuda.empty_cache()
+    log("timing the INT4 weight-only GEMV")
+    int4 = time_int4(torch, pda)
 
     step_s = r8["step_ms"] * 1e-3
     attn_s = r8["attn_ms"] * 1e-3
@@ -484,6 +569,7 @@ def main():
         "tag_check": tracker,
         "page_pool": time_page_pool(pda, np),
         "hbm_read_ceiling": ceiling,
+        "int4_gemv": int4,
         "step_ms_with_call_events": r8["step_ms_with_call_events"],
         "kv_GBps_attn": kv8 / attn_s / 1e9,
         "wall_ms_per_step": r8["wall_ms_per_step"],

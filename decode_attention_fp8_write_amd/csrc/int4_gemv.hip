@@ -17,9 +17,11 @@
 // token of the batch held in registers.
 //
 // Mapping. A workgroup of four waves owns 16 output rows, four per wave.
-// Lane l of a wave takes 16-element chunks l, l+64, ... of k (two packed
-// words per row and chunk, one 8-byte load), so the wave reads 512 contiguous
-// bytes of each row per step. A chunk lies inside one 128-element scale group.
+// Lane l of a wave takes chunks l, l+64, ... of k, 32 elements each (one
+// 16-byte load per row) for up to two tokens, 16 elements (8 bytes) for more,
+// where the activations take the registers; so the wave reads 1 KB or 512 B
+// of each row per load instruction, and several chunks' loads are issued
+// before their use. A chunk lies inside one 128-element scale group.
 //
 // Unpacking without integer-to-float conversions: a code u' = q + 8 in
 // [0, 15] (the two's-complement code with its top bit flipped) put into the
@@ -84,7 +86,11 @@ __global__ __launch_bounds__(64 * kWaves) void int4_gemv_kernel(
   const int wave = threadIdx.x >> 6;
   const int row0 = blockIdx.x * kRowsPerBlock + wave * kRowsPerWave;
   const int tok0 = blockIdx.y * kMaxTok;
-  const int chunks = k / 16;
+  // CW packed words (8*CW elements) per lane and chunk: 16-byte weight loads
+  // where few tokens leave registers to spare, 8-byte loads otherwise
+  constexpr int CW = MT <= 2 ? 4 : 2;
+  constexpr int CH = 8 * CW;
+  const int chunks = k / CH;
   const int words = k / 8;
   const int groups = k / kGroup;
 
@@ -108,49 +114,72 @@ __global__ __launch_bounds__(64 * kWaves) void int4_gemv_kernel(
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[r][t] = 0.0f;
 
-  for (int c = lane; c < chunks; c += 64) {
-    uint2 wq[kRowsPerWave];
-    float sc[kRowsPerWave];
+  // U chunks per lane per step, all their loads issued before any use, so
+  // enough bytes are in flight to cover HBM latency with few waves per CU
+  constexpr int U = MT <= 2 ? 4 : (MT == 4 ? 2 : 1);
+  for (int c0 = lane; c0 < chunks; c0 += 64 * U) {
+    uint32_t wq[U][kRowsPerWave][CW];
+    float sc[U][kRowsPerWave];
+    uint4 xv[U][MT][CW];
 #pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r) {
-      wq[r] = *reinterpret_cast<const uint2*>(wr[r] + 2 * c);
-      sc[r] = bf16_bits_to_f32(sr[r][c / (kGroup / 16)]);
-    }
-    // activation pairs and -136 * sum x of the chunk, per token
-    uint32_t xp[MT][8];
-    float base[MT];
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 64 * u;
+      if (c < chunks) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const uint4* xs = reinterpret_cast<const uint4*>(xt[t] + 16 * c);
-      const uint4 a = xs[0], b = xs[1];
-      pair_up(a, xp[t]);
-      pair_up(b, xp[t] + 4);
-      float s = 0.0f;
-      s = dot2(a.x, kOnes, s);
-      s = dot2(a.y, kOnes, s);
-      s = dot2(a.z, kOnes, s);
-      s = dot2(a.w, kOnes, s);
-      s = dot2(b.x, kOnes, s);
-      s = dot2(b.y, kOnes, s);
-      s = dot2(b.z, kOnes, s);
-      s = dot2(b.w, kOnes, s);
-      base[t] = -136.0f * s;
-    }
+        for (int r = 0; r < kRowsPerWave; ++r) {
+          if constexpr (CW == 4) {
+            const uint4 v = *reinterpret_cast<const uint4*>(wr[r] + CW * c);
+            wq[u][r][0] = v.x; wq[u][r][1] = v.y; wq[u][r][2] = v.z; wq[u][r][3] = v.w;
+          } else {
+            const uint2 v = *reinterpret_cast<const uint2*>(wr[r] + CW * c);
+            wq[u][r][0] = v.x; wq[u][r][1] = v.y;
+          }
+          sc[u][r] = bf16_bits_to_f32(sr[r][c / (kGroup / CH)]);
+        }
 #pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r) {
-      const uint32_t v0 = wq[r].x ^ 0x88888888u, v1 = wq[r].y ^ 0x88888888u;
-      uint32_t wb[8];
+        for (int t = 0; t < MT; ++t) {
+          const uint4* xs = reinterpret_cast<const uint4*>(xt[t] + CH * c);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        wb[j] = ((v0 >> (4 * j)) & 0x000F000Fu) | kMagic;
-        wb[4 + j] = ((v1 >> (4 * j)) & 0x000F000Fu) | kMagic;
+          for (int i = 0; i < CW; ++i) xv[u][t][i] = xs[i];
+        }
       }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + 64 * u >= chunks) break;
+      // activation pairs and -136 * sum x of the chunk, per token
+      uint32_t xp[MT][4 * CW];
+      float base[MT];
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
-        float d = base[t];
+        float s = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) d = dot2(wb[i], xp[t][i], d);
-        acc[r][t] = __builtin_fmaf(d, sc[r], acc[r][t]);
+        for (int i = 0; i < CW; ++i) {
+          const uint4 a = xv[u][t][i];
+          pair_up(a, xp[t] + 4 * i);
+          s = dot2(a.x, kOnes, s);
+          s = dot2(a.y, kOnes, s);
+          s = dot2(a.z, kOnes, s);
+          s = dot2(a.w, kOnes, s);
+        }
+        base[t] = -136.0f * s;
+      }
+#pragma unroll
+      for (int r = 0; r < kRowsPerWave; ++r) {
+        uint32_t wb[4 * CW];
+#pragma unroll
+        for (int i = 0; i < CW; ++i) {
+          const uint32_t v = wq[u][r][i] ^ 0x88888888u;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) wb[4 * i + j] = ((v >> (4 * j)) & 0x000F000Fu) | kMagic;
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          float d = base[t];
+#pragma unroll
+          for (int i = 0; i < 4 * CW; ++i) d = dot2(wb[i], xp[t][i], d);
+          acc[r][t] = __builtin_fmaf(d, sc[u][r], acc[r][t]);
+        }
       }
     }
   }
@@ -186,7 +215,7 @@ extern "C" int int4_gemv_bf16(const void* x, const uint32_t* w, const void* scal
   if (m == 0 || n == 0) return PDA_OK;
   if (k == 0) return PDA_ERR_UNSUPPORTED;
   if (!x || !w || !scale || !y) return PDA_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(x) & 15) != 0 || (reinterpret_cast<uintptr_t>(w) & 7) != 0 ||
+  if ((reinterpret_cast<uintptr_t>(x) & 15) != 0 || (reinterpret_cast<uintptr_t>(w) & 15) != 0 ||
       (reinterpret_cast<uintptr_t>(scale) & 1) != 0 || (reinterpret_cast<uintptr_t>(y) & 3) != 0)
     return PDA_ERR_INVALID_ARG;
   const int64_t blocks = ((int64_t)n + kRowsPerBlock - 1) / kRowsPerBlock;

@@ -24,7 +24,7 @@ extern "C" {
 /*
  * int4_gemv_bf16 — y[i][c] = sum_kk x[i][kk] * q[c][kk] * scale[c][kk / 128]
  *  x      device bf16 [m][k], 16-byte aligned (activations of m tokens).
- *  w      device uint32 [n][k / 8], 8-byte aligned: code j (bits 4j..4j+3,
+ *  w      device uint32 [n][k / 8], 16-byte aligned: code j (bits 4j..4j+3,
  *         two's complement, -8..7) of word kk / 8 of row c is q[c][kk] for
  *         kk = 8 * word + j.
  *  scale  device bf16 [n][k / 128], 2-byte aligned.
