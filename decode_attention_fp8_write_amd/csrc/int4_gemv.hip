@@ -11,10 +11,10 @@
 // off"). The format is not on the pages; the one taken here is stated in
 // include/pda_int4.h.
 //
-// Decode batches are small (one to a few dozen tokens), so the kernel is a
-// streaming dot-product kernel on the vector ALUs, not a matrix-core tile
-// loop: each weight byte is read from HBM once per launch and used by every
-// token of the batch held in registers.
+// Decode batches are small (one to a few dozen tokens). One token takes a
+// streaming dot-product kernel on the vector ALUs; two and more take a
+// matrix-core kernel (below) whose products are nearly free, so both are
+// limited by unpacking the codes and by moving bytes, not by arithmetic.
 //
 // Mapping. A workgroup of four waves owns 16 output rows, four per wave.
 // Lane l of a wave takes chunks l, l+64, ... of k, 32 elements each (one
@@ -37,8 +37,8 @@
 // ((word >> 4j) & 0x000F000F), so activations are paired the same way:
 // (x_j, x_{j+4}) by one byte permute per pair.
 //
-// Tokens: a launch handles up to kMaxTok tokens per grid row (grid.y covers
-// larger batches, each grid row streaming the weights again).
+// Tokens (vector-ALU kernel): up to kMaxTok tokens per grid row; grid.y
+// covers larger batches, each grid row streaming the weights again.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -202,6 +202,156 @@ __global__ __launch_bounds__(64 * kWaves) void int4_gemv_kernel(
         y[(int64_t)(tok0 + t) * n + row0 + r] = acc[r][t];
 }
 
+// ---- matrix-core path for two or more tokens ---------------------------
+// D[token][row] = sum_k x[token][k] W[row][k] on v_mfma_f32_16x16x32_bf16:
+// A = activations (16 tokens of a tile), B = unpacked codes (16 rows), both
+// in the same permuted k order inside each 32-wide step (element 2j is k j,
+// element 2j+1 is k j+4 of the lane's 8), which the sum does not see. Lane
+// (c, g) of a wave holds, for k-step s of scale group G, words 4g + s of
+// the group in row c (its 16 bytes of the group are one load) and the
+// activations of the same 8 k. A second product against a constant 136
+// operand gives 136 * sum x of the same k, subtracted at the group's end
+// before the group scale: fresh accumulators per group, one fma per output.
+// A workgroup owns 32 rows (two 16-row tiles) and up to 32 tokens (grid
+// rows of 32 tokens run side by side and share the weights through the
+// caches); its four waves take every fourth scale group and meet in LDS at
+// the end.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kRT = 2;              // 16-row tiles per workgroup
+constexpr int kMfmaRows = 16 * kRT;
+constexpr int kMfmaTok = 32;        // tokens per grid row (two 16-token tiles)
+constexpr uint32_t k136 = 0x43084308u;   // bf16 pair (136.0, 136.0)
+// batches from this many tokens take the matrix-core kernel
+constexpr int kMfmaMinTokens = 2;
+
+template <int TILES>
+__global__ __launch_bounds__(256) void int4_gemm_mfma_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ w,
+    const uint16_t* __restrict__ scale, int m, int n, int k, float* __restrict__ y) {
+  __shared__ float red[3][TILES * kRT * 4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int row0 = blockIdx.x * kMfmaRows;
+  const int tok0 = blockIdx.y * kMfmaTok;
+  const int groups = k / kGroup;
+
+  // out-of-range rows and tokens read row n-1 / token m-1 and are not stored
+  const uint32_t* wr[kRT];
+  const uint16_t* sr[kRT];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    const int row = min(row0 + 16 * rt + c, n - 1);
+    wr[rt] = w + (int64_t)row * (k / 8) + 4 * g;
+    sr[rt] = scale + (int64_t)row * groups;
+  }
+  const uint16_t* xr[TILES];
+#pragma unroll
+  for (int t = 0; t < TILES; ++t)
+    xr[t] = x + (int64_t)min(tok0 + 16 * t + c, m - 1) * k + 32 * g;
+
+  const uint4 c136 = make_uint4(k136, k136, k136, k136);
+  const bf16x8_t b136 = __builtin_bit_cast(bf16x8_t, c136);
+  f32x4_t yacc[TILES][kRT];
+#pragma unroll
+  for (int t = 0; t < TILES; ++t)
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) yacc[t][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // U groups per wave and step, their loads issued before any use
+  constexpr int U = TILES == 1 ? 4 : 2;
+  for (int g0 = wave; g0 < groups; g0 += 4 * U) {
+    uint4 wv[U][kRT];
+    float sc[U][kRT];
+    uint4 xv[U][TILES][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int gi = g0 + 4 * u;
+      if (gi < groups) {
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) {
+          wv[u][rt] = *reinterpret_cast<const uint4*>(wr[rt] + 16 * gi);
+          sc[u][rt] = bf16_bits_to_f32(sr[rt][gi]);
+        }
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            xv[u][t][s] = *reinterpret_cast<const uint4*>(xr[t] + kGroup * gi + 8 * s);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (g0 + 4 * u >= groups) break;
+      f32x4_t am[TILES][kRT], ac[TILES];
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        ac[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) am[t][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8_t bw[kRT];
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) {
+          const uint4 q = wv[u][rt];
+          const uint32_t word = s == 0 ? q.x : s == 1 ? q.y : s == 2 ? q.z : q.w;
+          const uint32_t v = word ^ 0x88888888u;
+          const uint4 d = make_uint4((v & 0x000F000Fu) | kMagic, ((v >> 4) & 0x000F000Fu) | kMagic,
+                                     ((v >> 8) & 0x000F000Fu) | kMagic,
+                                     ((v >> 12) & 0x000F000Fu) | kMagic);
+          bw[rt] = __builtin_bit_cast(bf16x8_t, d);
+        }
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) {
+          uint32_t p[4];
+          pair_up(xv[u][t][s], p);
+          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(p[0], p[1], p[2], p[3]));
+#pragma unroll
+          for (int rt = 0; rt < kRT; ++rt)
+            am[t][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw[rt], am[t][rt], 0, 0, 0);
+          ac[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b136, ac[t], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            yacc[t][rt][r] =
+                __builtin_fmaf(am[t][rt][r] - ac[t][r], sc[u][rt], yacc[t][rt][r]);
+    }
+  }
+
+  // waves 1..3 hand their partial sums to wave 0
+  if (wave > 0) {
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave - 1][(t * kRT + rt) * 4 + r][lane] = yacc[t][rt][r];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int t = 0; t < TILES; ++t)
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = (t * kRT + rt) * 4 + r;
+        const float v = yacc[t][rt][r] + red[0][i][lane] + red[1][i][lane] + red[2][i][lane];
+        const int tok = tok0 + 16 * t + 4 * g + r;
+        const int row = row0 + 16 * rt + c;
+        if (tok < m && row < n) y[(int64_t)tok * n + row] = v;
+      }
+}
+
 }  // namespace
 }  // namespace pda
 
@@ -221,9 +371,20 @@ extern "C" int int4_gemv_bf16(const void* x, const uint32_t* w, const void* scal
   const int64_t blocks = ((int64_t)n + kRowsPerBlock - 1) / kRowsPerBlock;
   const int64_t tok_blocks = ((int64_t)m + kMaxTok - 1) / kMaxTok;
   if (blocks > 0x7FFFFFFF || tok_blocks > 65535) return PDA_ERR_UNSUPPORTED;
+  hipStream_t s = as_stream(stream);
+  const auto* xb0 = static_cast<const uint16_t*>(x);
+  const auto* sb0 = static_cast<const uint16_t*>(scale);
+  if (m >= kMfmaMinTokens) {
+    const dim3 g2((unsigned)(((int64_t)n + kMfmaRows - 1) / kMfmaRows),
+                  (unsigned)(((int64_t)m + kMfmaTok - 1) / kMfmaTok));
+    if (m <= 16)
+      hipLaunchKernelGGL(int4_gemm_mfma_kernel<1>, g2, dim3(256), 0, s, xb0, w, sb0, m, n, k, y);
+    else
+      hipLaunchKernelGGL(int4_gemm_mfma_kernel<2>, g2, dim3(256), 0, s, xb0, w, sb0, m, n, k, y);
+    return launch_status();
+  }
   const dim3 grid((unsigned)blocks, (unsigned)tok_blocks);
   const dim3 block(64 * kWaves);
-  hipStream_t s = as_stream(stream);
   const int mt = m < kMaxTok ? m : kMaxTok;
   const auto* xb = static_cast<const uint16_t*>(x);
   const auto* sb = static_cast<const uint16_t*>(scale);

@@ -3,19 +3,22 @@ oracle's fp64 sum.
 
 Inputs: bf16 activations N(0, 1) with exact zeros and negative zeros mixed
 in, uniformly random packed words (every 4-bit code), bf16 scales of both
-signs. Shapes span ragged row counts (not multiples of the 16 rows of a
-workgroup), token counts from 1 to 17 (one to three token blocks of 8) and
-k from one scale group to 8192.
+signs. Shapes span ragged row counts (not multiples of the 16 or 32 rows
+of a workgroup), token counts from 1 (vector-ALU kernel) to 100 (matrix-core
+kernel: partial 16-token tiles, two grid rows of 64 tokens) and k from one
+scale group to 8192.
 
 Tolerance, from the kernel's arithmetic: every term enters an fp32 chain
 whose partial sums are bounded by 280 * sum|x| * |scale| per 16-element
 chunk (codes are offset by 136 and the offset is subtracted at the head of
 the chain), with under 8192 roundings on any path, so
 |y - exact| <= 8192 * 2^-24 * sum_k |x_k| * |scale_k|; on top, the
-root-mean-square error over all outputs must stay under 2e-6 of the
+root-mean-square error over all outputs must stay under 1e-5 of the
 outputs' own root mean square (a statistical guard: measured at most
-2.6e-7 on these cases, while a single wrong code moves an output by about
-|x| * |scale|, ~1e-3 of it).
+3e-7 for the vector-ALU kernel and 1.6e-6 for the matrix-core kernel,
+whose group sums cancel the 136 offset between two fp32 accumulators,
+while a single wrong code moves an output by about |x| * |scale|, ~1e-3
+of it).
 """
 import numpy as np
 import pytest
@@ -70,11 +73,12 @@ def _compare(got, ref, bound, what):
     assert (err <= bound).all(), f"{what}: error above the bound at {worst}"
     rel = np.sqrt((err ** 2).mean()) / max(np.sqrt((ref ** 2).mean()), 1e-30)
     log(f"{what}: rms rel {rel:.3e}")
-    assert rel <= 2e-6, f"{what}: rms relative error {rel:.3e}"
+    assert rel <= 1e-5, f"{what}: rms relative error {rel:.3e}"
 
 
 CASES = [(1, 16, 128), (1, 100, 384), (3, 37, 1024), (4, 64, 2048), (5, 33, 640),
-         (8, 50, 8192), (13, 20, 256), (17, 7, 128), (2, 1, 1152)]
+         (8, 50, 8192), (13, 20, 256), (17, 7, 128), (2, 1, 1152), (40, 24, 256),
+         (64, 33, 512), (100, 9, 128), (16, 32, 4096)]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"m{c[0]}_n{c[1]}_k{c[2]}")
@@ -87,7 +91,7 @@ def test_int4_gemv_parity(gpu, case):
     _compare(got, ref, _bound(x, s, np.arange(n)), f"m{m} n{n} k{k}")
 
 
-@pytest.mark.parametrize("m", [1, 8])
+@pytest.mark.parametrize("m", [1, 8, 64])
 def test_int4_gemv_full_size_sampled(gpu, m):
     """The measured shape, 8192 x 8192 weights: every output computed on the
     GPU, 96 sampled columns (first and last included) by the oracle."""
