@@ -31,9 +31,11 @@ extern "C" {
  *  m, n, k  tokens, output rows, inputs; k a multiple of 128.
  *  group  must be 128 (the scale group length).
  *  y      device fp32 [m][n], 4-byte aligned; written, never read.
- * Arithmetic: products and sums in fp32 (bf16 dot-product pairs), one fp32
- * accumulator per output; the result differs from the exact sum by at most
- * a few dozen fp32 roundings of sum_kk |x[i][kk]| * 144 * |scale|.
+ * Arithmetic: the codes enter as bf16 values q + 136 (exact) and the 136
+ * offset is subtracted per 128-input group in fp32; one token runs on bf16
+ * dot-product pairs, two and more on 16x16x32 bf16 matrix-core products,
+ * both with fp32 accumulation. The result differs from the exact sum by at
+ * most 8192 * 2^-24 * sum_kk |x[i][kk]| * |scale[c][kk / 128]|.
  * Asynchronous on `stream`; nothing is allocated. Returns 0,
  * PDA_ERR_INVALID_ARG (1) for negative sizes, NULL or misaligned pointers,
  * PDA_ERR_UNSUPPORTED (2) for group != 128, k not a positive multiple of 128
