@@ -214,8 +214,10 @@ __global__ __launch_bounds__(64 * kWaves) void int4_gemv_kernel(
 // before the group scale: fresh accumulators per group, one fma per output.
 // A workgroup owns 32 rows (two 16-row tiles) and up to 32 tokens (grid
 // rows of 32 tokens run side by side and share the weights through the
-// caches); its four waves take every fourth scale group and meet in LDS at
-// the end.
+// caches); its NW waves take every NW-th scale group and meet in LDS at the
+// end: eight waves for one 16-token tile, four for two, whose registers
+// leave room for fewer waves (measured: eight waves 3-4 us faster up to 16
+// tokens, even at 32, slower at 64).
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -226,11 +228,11 @@ constexpr uint32_t k136 = 0x43084308u;   // bf16 pair (136.0, 136.0)
 // batches from this many tokens take the matrix-core kernel
 constexpr int kMfmaMinTokens = 2;
 
-template <int TILES>
-__global__ __launch_bounds__(256) void int4_gemm_mfma_kernel(
+template <int TILES, int NW>
+__global__ __launch_bounds__(64 * NW) void int4_gemm_mfma_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ w,
     const uint16_t* __restrict__ scale, int m, int n, int k, float* __restrict__ y) {
-  __shared__ float red[3][TILES * kRT * 4][64];
+  __shared__ float red[NW - 1][TILES * kRT * 4][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -262,13 +264,13 @@ __global__ __launch_bounds__(256) void int4_gemm_mfma_kernel(
 
   // U groups per wave and step, their loads issued before any use
   constexpr int U = TILES == 1 ? 4 : 2;
-  for (int g0 = wave; g0 < groups; g0 += 4 * U) {
+  for (int g0 = wave; g0 < groups; g0 += NW * U) {
     uint4 wv[U][kRT];
     float sc[U][kRT];
     uint4 xv[U][TILES][4];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int gi = g0 + 4 * u;
+      const int gi = g0 + NW * u;
       if (gi < groups) {
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) {
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(256) void int4_gemm_mfma_kernel(
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (g0 + 4 * u >= groups) break;
+      if (g0 + NW * u >= groups) break;
       f32x4_t am[TILES][kRT], ac[TILES];
 #pragma unroll
       for (int t = 0; t < TILES; ++t) {
@@ -327,7 +329,7 @@ __global__ __launch_bounds__(256) void int4_gemm_mfma_kernel(
     }
   }
 
-  // waves 1..3 hand their partial sums to wave 0
+  // the other waves hand their partial sums to wave 0
   if (wave > 0) {
 #pragma unroll
     for (int t = 0; t < TILES; ++t)
@@ -345,7 +347,9 @@ __global__ __launch_bounds__(256) void int4_gemm_mfma_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = (t * kRT + rt) * 4 + r;
-        const float v = yacc[t][rt][r] + red[0][i][lane] + red[1][i][lane] + red[2][i][lane];
+        float v = yacc[t][rt][r];
+#pragma unroll
+        for (int o = 0; o < NW - 1; ++o) v += red[o][i][lane];
         const int tok = tok0 + 16 * t + 4 * g + r;
         const int row = row0 + 16 * rt + c;
         if (tok < m && row < n) y[(int64_t)tok * n + row] = v;
@@ -378,9 +382,11 @@ extern "C" int int4_gemv_bf16(const void* x, const uint32_t* w, const void* scal
     const dim3 g2((unsigned)(((int64_t)n + kMfmaRows - 1) / kMfmaRows),
                   (unsigned)(((int64_t)m + kMfmaTok - 1) / kMfmaTok));
     if (m <= 16)
-      hipLaunchKernelGGL(int4_gemm_mfma_kernel<1>, g2, dim3(256), 0, s, xb0, w, sb0, m, n, k, y);
+      hipLaunchKernelGGL((int4_gemm_mfma_kernel<1, 8>), g2, dim3(64 * 8), 0, s, xb0, w, sb0, m,
+                         n, k, y);
     else
-      hipLaunchKernelGGL(int4_gemm_mfma_kernel<2>, g2, dim3(256), 0, s, xb0, w, sb0, m, n, k, y);
+      hipLaunchKernelGGL((int4_gemm_mfma_kernel<2, 4>), g2, dim3(64 * 4), 0, s, xb0, w, sb0, m,
+                         n, k, y);
     return launch_status();
   }
   const dim3 grid((unsigned)blocks, (unsigned)tok_blocks);
