@@ -48,6 +48,8 @@ def _load():
     lib.oracle_e4m3_decode.restype = f64
     lib.oracle_e4m3_encode.argtypes = [f32]
     lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_e4m3_encode_brute.argtypes = [f32]
+    lib.oracle_e4m3_encode_brute.restype = ctypes.c_uint8
     lib.oracle_e4m3_encode_closed.argtypes = [f32]
     lib.oracle_e4m3_encode_closed.restype = ctypes.c_uint8
     lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
@@ -97,6 +99,10 @@ def e4m3_decode(code: int) -> float:
 
 def e4m3_encode(x: float) -> int:
     return _load().oracle_e4m3_encode(float(x))
+
+
+def e4m3_encode_brute(x: float) -> int:
+    return _load().oracle_e4m3_encode_brute(float(x))
 
 
 def e4m3_encode_closed(x: float) -> int:

@@ -34,8 +34,9 @@ double oracle_e4m3_decode(uint8_t code) {
  * distances that decide a comparison are exact in fp64: near a tie, |x| and
  * the two neighbouring code values lie within a few binades of each other,
  * so |x| - v needs at most 24 + 5 significant bits; far candidates differ by
- * factors no rounding can flip. */
-uint8_t oracle_e4m3_encode(float x) {
+ * factors no rounding can flip. This is the definition the faster search
+ * below is checked against. */
+uint8_t oracle_e4m3_encode_brute(float x) {
   uint8_t sign = signbit(x) ? 0x80 : 0x00;
   if (isnan(x)) return (uint8_t)(0x7F | sign);
   double a = fabs((double)x);
@@ -50,6 +51,34 @@ uint8_t oracle_e4m3_encode(float x) {
     }
   }
   return (uint8_t)(best | sign);
+}
+
+/* The values of codes 0x00..0x7E, which increase with the code. */
+static double g_e4m3_values[127];
+static pthread_once_t g_e4m3_once = PTHREAD_ONCE_INIT;
+
+static void e4m3_values_init(void) {
+  for (int c = 0; c <= 0x7E; ++c) g_e4m3_values[c] = oracle_e4m3_decode((uint8_t)c);
+}
+
+/* The same nearest code, found by bisection instead of a scan: since the
+ * values increase with the code, |x| lies between code lo (largest value
+ * <= |x|) and lo + 1, and the nearer of the two wins, the even one on a
+ * tie. The two distances are exact or far from equal, as above. */
+uint8_t oracle_e4m3_encode(float x) {
+  uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  if (isnan(x)) return (uint8_t)(0x7F | sign);
+  double a = fabs((double)x);
+  if (a >= 448.0) return (uint8_t)(0x7E | sign);
+  pthread_once(&g_e4m3_once, e4m3_values_init);
+  int lo = 0, hi = 0x7E; /* value(lo) = 0 <= a < 448 = value(hi) */
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (g_e4m3_values[mid] <= a) lo = mid; else hi = mid;
+  }
+  double d_lo = a - g_e4m3_values[lo], d_hi = g_e4m3_values[hi] - a;
+  int c = (d_lo < d_hi) ? lo : (d_hi < d_lo) ? hi : ((lo & 1) == 0 ? lo : hi);
+  return (uint8_t)(c | sign);
 }
 
 /* Closed form: codes are equally spaced inside each binade and the spacing

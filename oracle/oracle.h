@@ -44,6 +44,10 @@ double oracle_e4m3_decode(uint8_t code);          /* NaN for 0x7F / 0xFF   */
  * even code, then the sign bit of x is ORed in (so -0 and negative underflow
  * give 0x80). */
 uint8_t oracle_e4m3_encode(float x);
+/* The same definition computed by a scan over all 127 candidates (the form
+ * the definition states); oracle_e4m3_encode finds the same code by bisection
+ * over the increasing code values and is checked against this one. */
+uint8_t oracle_e4m3_encode_brute(float x);
 /* Closed-form bit-level encoder; a cross-check of oracle_e4m3_encode only. */
 uint8_t oracle_e4m3_encode_closed(float x);
 float oracle_bf16_to_f32(uint16_t bits);

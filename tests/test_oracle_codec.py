@@ -115,6 +115,7 @@ def test_p2_round_trip():
 ])
 def test_p3_ties_and_saturation(x, code):
     assert oracle.e4m3_encode(x) == code
+    assert oracle.e4m3_encode_brute(x) == code
     assert oracle.e4m3_encode_closed(x) == code
 
 
@@ -128,6 +129,27 @@ def test_p4_closed_form_equals_brute_force_all_bf16():
         assert oracle.e4m3_encode(x) == oracle.e4m3_encode_closed(x), x
 
 
+def test_bisection_equals_brute_force_all_bf16():
+    """The encoder the oracle uses (bisection over the increasing code
+    values) and the definition's scan over all 127 candidates agree on every
+    bf16 pattern."""
+    for x in _all_bf16_f32():
+        assert oracle.e4m3_encode(x) == oracle.e4m3_encode_brute(x), x
+
+
+def test_bisection_equals_brute_force_random_f32():
+    """... and on fp32 quotients of every magnitude (kv_write encodes x /
+    scale, which is rarely a bf16 value), including fp32 subnormals and
+    values just below and above the saturation bound."""
+    rng = np.random.default_rng(11)
+    n = 60000
+    xs = (rng.standard_normal(n) * np.exp2(rng.uniform(-150, 10, n))).astype(np.float32)
+    xs = np.concatenate([xs, np.float32(448) * (1 + rng.uniform(-1e-3, 1e-3, 2000)).astype(
+        np.float32), rng.integers(0, 1 << 23, 2000, dtype=np.uint32).view(np.float32)])
+    for x in xs:
+        assert oracle.e4m3_encode(x) == oracle.e4m3_encode_brute(x), x
+
+
 def test_p4_midpoints_and_neighbours():
     v = oracle.e4m3_decode_all()[:0x7F]
     mids = (v[:-1] + v[1:]) / 2.0
@@ -138,6 +160,7 @@ def test_p4_midpoints_and_neighbours():
                   np.nextafter(m32, np.float32(1000))):
             for s in (x, -x):
                 assert oracle.e4m3_encode(s) == oracle.e4m3_encode_closed(s)
+                assert oracle.e4m3_encode(s) == oracle.e4m3_encode_brute(s)
         lo = int(np.searchsorted(v, m) - 1)
         even = lo if lo % 2 == 0 else lo + 1
         assert oracle.e4m3_encode(m32) == even
