@@ -314,8 +314,7 @@ def cpu_baseline(batch, data, host_scales, target_s=12.0):
 
     import oracle
     import synth
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_helpers import oracle_subset
+    from oracle.harness import oracle_subset
 
     cfg = batch.cfg
     nthreads = os.cpu_count() or 1
@@ -468,7 +467,7 @@ def main():
 
     import synth
     import decode_attention_fp8_write_amd as pda
-    from decode_attention_fp8_write_amd import workload
+    from synth import device as workload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     pda.load()

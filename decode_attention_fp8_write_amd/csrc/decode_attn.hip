@@ -1205,6 +1205,30 @@ int blocks_per_cu(kernel_t k, size_t lds) {
   return nb;
 }
 
+// Raise a partial kernel's dynamic LDS limit to what `lds` needs, once per
+// (kernel, device); false if the runtime refuses it.
+bool allow_lds(kernel_t k, size_t lds) {
+  if (lds <= 65536) return true;
+  static std::mutex mu;
+  static kernel_t keys[64];
+  static int devs[64];
+  static int n = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < n; ++i)
+    if (keys[i] == k && devs[i] == dev) return true;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+    return false;
+  if (n < 64) {
+    keys[n] = k;
+    devs[n] = dev;
+    ++n;
+  }
+  return true;
+}
+
 }  // namespace
 
 int device_cu_count() {
@@ -1226,6 +1250,7 @@ int device_cu_count() {
 // Latent (MFMA) path, decode_attn_latent.hip.
 bool latent_supported(const pda_attn_shape& sh);
 size_t latent_workspace_bytes(const pda_attn_shape& sh, int32_t max_seq_len);
+size_t latent_min_workspace_bytes(const pda_attn_shape& sh);
 int latent_launch(const pda_attn_shape& sh, const void* q, const void* k_cache,
                   const float* token_scale, const int32_t* block_table, const int32_t* seq_lens,
                   int32_t max_seq_len, const int32_t* verdict, void* workspace,
@@ -1250,12 +1275,16 @@ extern "C" size_t paged_decode_attn_workspace_bytes(const pda_attn_shape* shape,
   return header_bytes(sh.num_seqs) + (size_t)items * item_bytes(sh);
 }
 
-extern "C" int paged_decode_attn(const pda_attn_shape* shape, const void* q, const void* k_cache,
-                                 const void* v_cache, const float* k_scale,
-                                 const float* v_scale, const int32_t* block_table,
-                                 const int32_t* seq_lens, int32_t max_seq_len,
-                                 const int32_t* verdict, void* workspace,
-                                 size_t workspace_bytes, float* out, void* stream) {
+namespace pda {
+namespace {
+
+// The whole call behind both entry points: shape checks, then the partial
+// and combine launches with the given workspace.
+int attn_call(const pda_attn_shape* shape, const void* q, const void* k_cache,
+              const void* v_cache, const float* k_scale, const float* v_scale,
+              const int32_t* block_table, const int32_t* seq_lens, int32_t max_seq_len,
+              const int32_t* verdict, void* workspace, size_t workspace_bytes, float* out,
+              void* stream) {
   int st = check_shape(shape);
   if (st != PDA_OK) return st;
   const pda_attn_shape& sh = *shape;
@@ -1310,6 +1339,9 @@ extern "C" int paged_decode_attn(const pda_attn_shape* shape, const void* q, con
                                           (fp8 ? 8192 : 0)) +
                       (fp8 ? (size_t)G * kD * 2 : (size_t)kWaves * ((ib + 15) & ~(size_t)15));
   const size_t lds = pbuf + (size_t)(kThreads + 1 + sh.num_seqs + 1) * sizeof(int);
+  // the per-sequence slot prefix lives in LDS too: past 64 KB (several
+  // thousand sequences) the kernel needs the larger dynamic LDS limit
+  if (!allow_lds(pk, lds)) return PDA_ERR_LAUNCH;
   const long long ml = max_seq_len > 0 ? max_seq_len : 1;
   const long long units_bound =
       (long long)sh.num_seqs * sh.num_kv_heads * (((ml + chunk - 1) / chunk + kWaves - 1) / kWaves);
@@ -1327,4 +1359,17 @@ extern "C" int paged_decode_attn(const pda_attn_shape* shape, const void* q, con
   hipLaunchKernelGGL(ck, dim3((unsigned)(sh.num_seqs * sh.num_kv_heads)), dim3(kThreads), 0, s, a,
                      (int)sh.page_size);
   return launch_status();
+}
+
+}  // namespace
+}  // namespace pda
+
+extern "C" int paged_decode_attn(const pda_attn_shape* shape, const void* q, const void* k_cache,
+                                 const void* v_cache, const float* k_scale,
+                                 const float* v_scale, const int32_t* block_table,
+                                 const int32_t* seq_lens, int32_t max_seq_len,
+                                 const int32_t* verdict, void* workspace,
+                                 size_t workspace_bytes, float* out, void* stream) {
+  return attn_call(shape, q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens,
+                   max_seq_len, verdict, workspace, workspace_bytes, out, stream);
 }

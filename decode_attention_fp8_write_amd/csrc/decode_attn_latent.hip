@@ -684,6 +684,11 @@ size_t latent_workspace_bytes(const pda_attn_shape& sh, int32_t max_seq_len) {
   return lat_header_bytes(sh.num_seqs) + slots * lat_slot_bytes(sh);
 }
 
+// Smallest workspace the call accepts: one partial per sequence plus one.
+size_t latent_min_workspace_bytes(const pda_attn_shape& sh) {
+  return lat_header_bytes(sh.num_seqs) + lat_slot_bytes(sh) * ((size_t)sh.num_seqs + 1);
+}
+
 int latent_launch(const pda_attn_shape& sh, const void* q, const void* k_cache,
                   const float* token_scale, const int32_t* block_table, const int32_t* seq_lens,
                   int32_t max_seq_len, const int32_t* verdict, void* workspace,
@@ -691,7 +696,7 @@ int latent_launch(const pda_attn_shape& sh, const void* q, const void* k_cache,
   (void)max_seq_len;
   const size_t hdr = lat_header_bytes(sh.num_seqs);
   const size_t slot = lat_slot_bytes(sh);
-  if (workspace_bytes < hdr + slot * ((size_t)sh.num_seqs + 1)) return PDA_ERR_WORKSPACE;
+  if (workspace_bytes < latent_min_workspace_bytes(sh)) return PDA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return PDA_ERR_INVALID_ARG;
   long long grid = device_cu_count();
   const long long fit = (long long)((workspace_bytes - hdr) / slot) - sh.num_seqs;

@@ -151,13 +151,16 @@ class PagePool:
     among pages in use (until the counter wraps). Free pages are kept on a
     stack: the most recently freed page is handed out first."""
 
-    def __init__(self, num_pages: int, rng: np.random.Generator,
-                 tag_start: int = 0):
+    def __init__(self, num_pages: int, rng: Optional[np.random.Generator] = None,
+                 tag_start: int = 0, order=None):
         self.num_pages = num_pages
         self.tags = np.zeros(num_pages, dtype=np.uint32)
         self.counter = int(tag_start) & 0xFFFFFFFF
-        # initial free stack in a seeded order; pop() takes from the end
-        self._free = [int(p) for p in rng.permutation(num_pages)[::-1]]
+        # initial free stack in a seeded order (or the given order of the
+        # first hand-outs); pop() takes from the end
+        if order is None:
+            order = rng.permutation(num_pages)
+        self._free = [int(p) for p in np.asarray(order)[::-1]]
 
     @property
     def num_free(self) -> int:
@@ -285,14 +288,24 @@ def make_q(cfg: Config, num_seqs: int) -> np.ndarray:
     return bf16_from_f32(q)
 
 
+def _tags_of(pool) -> np.ndarray:
+    t = pool.tags
+    return np.asarray(t() if callable(t) else t, dtype=np.uint32).copy()
+
+
 def make_batch(cid: int, lens=None, num_pages: Optional[int] = None,
                inject: Optional[int] = None, pool_factor: float = 1.2,
-               churn_rounds: int = 6) -> Batch:
+               churn_rounds: int = 6, pool_factory=None) -> Batch:
     """Build the page bookkeeping and queries of a workload.
 
     lens overrides the workload's lengths (for scaled-down parity runs).
     inject overrides the number of injected tag mismatches (default: 1 for
-    workload 1, floor(pages in use / 10000) for workload 5, else 0)."""
+    workload 1, floor(pages in use / 10000) for workload 5, else 0).
+    pool_factory(num_pages, order) -> pool replaces this module's PagePool
+    by another pool with the same interface (alloc(n) -> (pages, tags),
+    free(pages), num_free, num_pages, tags) whose first hand-outs follow
+    `order`, e.g. the library's own page pool; the seeded sequence of pool
+    operations is the same."""
     cfg = CONFIGS[cid]
     seq_lens = config_lengths(cfg) if lens is None else np.asarray(lens, np.int32)
     B = int(seq_lens.shape[0])
@@ -303,18 +316,19 @@ def make_batch(cid: int, lens=None, num_pages: Optional[int] = None,
     prng = rng_for(cfg.seed, _POOL)
     if cid == 5:
         P = num_pages or int(math.ceil(pool_factor * used / 64.0)) * 64
-        pool = PagePool(P, prng)
-        _churn(pool, cfg, prng, churn_rounds)
     else:
         P = num_pages or (64 if cid == 1 else max(used, 1))
-        pool = PagePool(P, prng)
+    order = prng.permutation(P)
+    pool = (pool_factory or (lambda n, o: PagePool(n, order=o)))(P, order)
+    if cid == 5:
+        _churn(pool, cfg, prng, churn_rounds)
     block_table = np.full((B, max_blocks), -1, dtype=np.int32)
     expected = np.zeros((B, max_blocks), dtype=np.uint32)
     for s in range(B):
         pages, tags = pool.alloc(npages[s])
         block_table[s, :npages[s]] = pages
         expected[s, :npages[s]] = tags
-    page_tags = pool.tags.copy()
+    page_tags = _tags_of(pool)
     if inject is None:
         inject = 1 if cid == 1 else (used // 10000 if cid == 5 else 0)
     injected = []
@@ -332,7 +346,7 @@ def make_batch(cid: int, lens=None, num_pages: Optional[int] = None,
                  q, max_blocks)
 
 
-def _churn(pool: PagePool, cfg: Config, rng: np.random.Generator,
+def _churn(pool, cfg: Config, rng: np.random.Generator,
            rounds: int) -> None:
     """Seeded rounds of handing out pages to short-lived sequences and freeing
     a random half of them, then freeing the rest, so the free stack the live

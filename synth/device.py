@@ -1,10 +1,12 @@
-"""Device-resident synthetic workloads for the benchmark and the GPU tests.
+"""Device-resident synthetic workloads for the benchmark, the smoke check
+and the GPU tests (harness side of the library's boundary).
 
 Builds one decode step's inputs on the GPU from the seeded generator in
-``synth`` (input generation only) using this package's own kernels: the
+``synth`` (input generation only) through the library's own calls: the
 context of every sequence is written into the paged cache with
 kv_write_fp8 / kv_write_bf16, exactly as a serving step would. Nothing here
-computes attention.
+computes any step of the path itself. Importing this module loads the
+library's Python binding; ``synth`` itself does not.
 """
 from __future__ import annotations
 
@@ -14,10 +16,10 @@ from typing import Optional
 import numpy as np
 
 import synth
-
-from . import (KV_BF16, KV_FP8_E4M3, SCALE_NONE, SCALE_PER_HEAD, SCALE_PER_TOKEN,
-               kv_write_bf16, kv_write_fp8, make_shape, paged_decode_attn,
-               paged_decode_attn_workspace_bytes, validate_page_tags)
+from decode_attention_fp8_write_amd import (
+    KV_BF16, KV_FP8_E4M3, SCALE_NONE, SCALE_PER_HEAD, SCALE_PER_TOKEN, kv_write_bf16,
+    kv_write_fp8, make_shape, paged_decode_attn, paged_decode_attn_workspace_bytes,
+    validate_page_tags)
 
 
 def _u16(torch, a: np.ndarray):

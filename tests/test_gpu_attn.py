@@ -239,7 +239,7 @@ def test_workload1_end_to_end(gpu):
     """Workload 1 as one decode step: write, validate (one injected mismatch
     aborts its sequence), attend; compared with the oracle on every row."""
     log("workload 1 end to end")
-    from decode_attention_fp8_write_amd import workload
+    from synth import device as workload
     from gpu_helpers import oracle_attn_subset, oracle_subset
     import oracle
     b = synth.make_batch(1)
@@ -258,3 +258,43 @@ def test_workload1_end_to_end(gpu):
         got = db.out.cpu().numpy()
         assert_attn_close(got, ref, f"workload 1 dtype {kv_dtype}")
         assert np.all(got[ver_ref != 0] == 0)
+
+
+@pytest.mark.parametrize("kv_dtype", [synth.KV_FP8, synth.KV_BF16])
+def test_many_short_sequences(gpu, kv_dtype):
+    """The largest batch the vector-ALU path takes: 16384 sequences of 1 to
+    48 tokens with the 64 x 8192 workload's heads (the per-sequence slot
+    prefix then needs over 64 KB of LDS per workgroup), every row compared.
+    K/V come from one seeded stream split by sequence (a per-sequence stream
+    for 16384 sequences costs more host time than the test itself)."""
+    import oracle
+    from synth import device as workload
+    from oracle.harness import oracle_attn_full, oracle_full_cache
+    log(f"16384 short sequences, dtype {kv_dtype}")
+    rng = np.random.default_rng(16384)
+    lens = rng.integers(1, 49, size=16384)
+    b = synth.make_batch(3, lens=lens)
+    cfg = b.cfg
+    T = int(lens.sum())
+    k = synth.bf16_from_f32(rng.standard_normal((T, cfg.num_kv_heads, cfg.head_dim_qk),
+                                                dtype=np.float32))
+    v = synth.bf16_from_f32(rng.standard_normal((T, cfg.num_kv_heads, cfg.head_dim_v),
+                                                dtype=np.float32))
+    cut = np.concatenate([[0], np.cumsum(lens)])
+    data = [(k[cut[s]:cut[s + 1]], v[cut[s]:cut[s + 1]]) for s in range(b.B)]
+    db = workload.build(b, kv_dtype, data=data)
+    db.alloc_workspace(split_tokens=0)
+    db.step(use_verdict=True)
+    torch.cuda.synchronize()
+    verdict = db.verdict.cpu().numpy()
+    assert np.all(verdict == 0)
+    got = db.out.cpu().numpy()
+    kc, vc, ts = oracle_full_cache(b, data, kv_dtype, db.host_scales)
+    elt = np.uint8 if kv_dtype == synth.KV_FP8 else np.uint16
+    assert np.array_equal(db.k_cache.cpu().numpy().view(elt), kc)
+    assert np.array_equal(db.v_cache.cpu().numpy().view(elt), vc)
+    want = oracle.validate_page_tags(b.page_tags, b.block_table, b.expected_tags,
+                                     b.seq_lens, cfg.page_size)
+    assert np.array_equal(verdict, want)
+    ref = oracle_attn_full(b, kc, vc, ts, kv_dtype, db.host_scales, verdict)
+    assert_attn_close(got, ref, f"16384 sequences dtype {kv_dtype}")

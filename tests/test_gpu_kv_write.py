@@ -120,7 +120,7 @@ def test_bf16_copy_and_skipped_slots(gpu):
 @pytest.mark.parametrize("kv_dtype", [synth.KV_FP8, synth.KV_BF16])
 def test_workload1_caches_bit_exact(gpu, kv_dtype):
     log(f"workload 1 cache build, dtype {kv_dtype}")
-    from decode_attention_fp8_write_amd import workload
+    from synth import device as workload
     from gpu_helpers import oracle_subset
     b = synth.make_batch(1)
     data = [b.kv(s) for s in range(b.B)]

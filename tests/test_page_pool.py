@@ -156,3 +156,20 @@ def test_reallocated_pages_fail_the_tag_check():
     verdict = oracle.validate_page_tags(pool.tags(), bt, et, np.int32(lens), S)
     first_reused = min(int(np.where(tables[1] == p)[0][0]) for p in newp)
     assert verdict.tolist() == [0, first_reused + 1, 0]
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_library_pool_replays_every_workload(cid):
+    """Every workload's page bookkeeping (block tables, expected tags, page
+    tags after injection), built once with the harness's pool and once with
+    the library's pda_pool_* driven through the same seeded operations: the
+    full-pool workload's six rounds of allocate/free churn included, the two
+    agree exactly."""
+    import decode_attention_fp8_write_amd as pda
+    pda.load()
+    a = synth.make_batch(cid)
+    b = synth.make_batch(cid, pool_factory=lambda n, o: pda.PagePool(n, initial_order=o))
+    assert np.array_equal(a.block_table, b.block_table)
+    assert np.array_equal(a.expected_tags, b.expected_tags)
+    assert np.array_equal(a.page_tags, b.page_tags)
+    assert a.injected == b.injected
