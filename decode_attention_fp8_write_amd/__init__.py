@@ -19,12 +19,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpda.so")
 
 (PDA_OK, PDA_ERR_INVALID_ARG, PDA_ERR_UNSUPPORTED, PDA_ERR_LAUNCH, PDA_ERR_WORKSPACE,
- PDA_ERR_POOL_EXHAUSTED) = range(6)
+ PDA_ERR_POOL_EXHAUSTED, PDA_ERR_SCRATCH) = range(7)
 KV_BF16, KV_FP8_E4M3 = 0, 1
 SCALE_NONE, SCALE_PER_HEAD, SCALE_PER_TOKEN = 0, 1, 2
 
 EXPORTS = ("kv_write_fp8", "kv_write_bf16", "kv_transcode_bf16_to_fp8", "validate_page_tags",
            "paged_decode_attn_workspace_bytes", "paged_decode_attn",
+           "paged_decode_attn_noalloc", "paged_decode_attn_noalloc_scratch_bytes",
            "pda_status_string", "pda_pool_create", "pda_pool_destroy", "pda_pool_alloc",
            "pda_pool_free", "pda_pool_tags", "pda_pool_num_free",
            "pda_hbm_read_probe", "pda_hbm_read_probe_sink_words", "int4_gemv_bf16")
@@ -76,6 +77,11 @@ def load(path: str | None = None):
     lib.paged_decode_attn.argtypes = [ctypes.POINTER(AttnShape), V, V, V, V, V, V, V, I32,
                                       V, V, ctypes.c_size_t, V, V]
     lib.paged_decode_attn.restype = ctypes.c_int
+    lib.paged_decode_attn_noalloc.argtypes = [ctypes.POINTER(AttnShape), V, V, V, V, V, V, V,
+                                              I32, V, V, V]
+    lib.paged_decode_attn_noalloc.restype = ctypes.c_int
+    lib.paged_decode_attn_noalloc_scratch_bytes.argtypes = []
+    lib.paged_decode_attn_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.pda_status_string.argtypes = [ctypes.c_int]
     lib.pda_status_string.restype = ctypes.c_char_p
     lib.pda_pool_create.argtypes = [I32, V, ctypes.c_uint32, I32, ctypes.POINTER(ctypes.c_void_p)]
@@ -216,6 +222,24 @@ def paged_decode_attn(shape: AttnShape, q, k_cache, v_cache, k_scale, v_scale, b
         workspace.numel() * workspace.element_size(), _ptr(out, elem=4, name="out"),
         _stream(stream))
     _check("paged_decode_attn", st)
+
+
+def paged_decode_attn_noalloc(shape: AttnShape, q, k_cache, v_cache, k_scale, v_scale,
+                              block_table, seq_lens, max_seq_len, verdict, out, stream=None):
+    """paged_decode_attn without a workspace: the library's fixed per-device
+    scratch holds the partials (calls on one device must not overlap)."""
+    elem = 1 if shape.kv_dtype == KV_FP8_E4M3 else 2
+    st = load().paged_decode_attn_noalloc(
+        ctypes.byref(shape), _ptr(q, elem=2, name="q"), _ptr(k_cache, elem=elem, name="k_cache"),
+        _ptr(v_cache, elem=elem, name="v_cache"), _ptr(k_scale, elem=4, name="k_scale"),
+        _ptr(v_scale, elem=4, name="v_scale"), _ptr(block_table, elem=4, name="block_table"),
+        _ptr(seq_lens, elem=4, name="seq_lens"), int(max_seq_len),
+        _ptr(verdict, elem=4, name="verdict"), _ptr(out, elem=4, name="out"), _stream(stream))
+    _check("paged_decode_attn_noalloc", st)
+
+
+def paged_decode_attn_noalloc_scratch_bytes() -> int:
+    return int(load().paged_decode_attn_noalloc_scratch_bytes())
 
 
 class PagePool:

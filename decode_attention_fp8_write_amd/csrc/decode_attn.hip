@@ -1361,6 +1361,34 @@ int attn_call(const pda_attn_shape* shape, const void* q, const void* k_cache,
   return launch_status();
 }
 
+// Fixed device scratch of the allocation-free entry point: one copy per
+// device (file scope, 256-byte aligned), never freed before the process
+// ends. Host code never uses the symbol itself as an address: the device
+// address of each device's copy is looked up once, with that device
+// current, and kept here.
+constexpr size_t kScratchBytes = (size_t)96 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+void* scratch_address() {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+// Smallest workspace a shape can run in (see paged_decode_attn_workspace_bytes).
+size_t min_workspace_bytes(const pda_attn_shape& sh) {
+  if (latent_supported(sh)) return latent_min_workspace_bytes(sh);
+  return header_bytes(sh.num_seqs) + (size_t)sh.num_seqs * sh.num_kv_heads * item_bytes(sh);
+}
+
 }  // namespace
 }  // namespace pda
 
@@ -1372,4 +1400,27 @@ extern "C" int paged_decode_attn(const pda_attn_shape* shape, const void* q, con
                                  size_t workspace_bytes, float* out, void* stream) {
   return attn_call(shape, q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens,
                    max_seq_len, verdict, workspace, workspace_bytes, out, stream);
+}
+
+extern "C" size_t paged_decode_attn_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" int paged_decode_attn_noalloc(const pda_attn_shape* shape, const void* q,
+                                         const void* k_cache, const void* v_cache,
+                                         const float* k_scale, const float* v_scale,
+                                         const int32_t* block_table, const int32_t* seq_lens,
+                                         int32_t max_seq_len, const int32_t* verdict,
+                                         float* out, void* stream) {
+  // host-side checks first: nothing below touches the device before they pass
+  int st = check_shape(shape);
+  if (st != PDA_OK) return st;
+  if (max_seq_len < 0) return PDA_ERR_INVALID_ARG;
+  if (shape->num_seqs == 0) return PDA_OK;
+  if (!q || !k_cache || !block_table || !seq_lens || !out) return PDA_ERR_INVALID_ARG;
+  if ((latent_supported(*shape) || valu_supported(*shape)) &&
+      min_workspace_bytes(*shape) > kScratchBytes)
+    return PDA_ERR_SCRATCH;
+  void* ws = scratch_address();
+  if (ws == nullptr) return PDA_ERR_LAUNCH;
+  return attn_call(shape, q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens,
+                   max_seq_len, verdict, ws, kScratchBytes, out, stream);
 }

@@ -9,6 +9,8 @@ extern "C" const char* pda_status_string(int status) {
     case PDA_ERR_LAUNCH: return "kernel launch failed";
     case PDA_ERR_WORKSPACE: return "workspace too small";
     case PDA_ERR_POOL_EXHAUSTED: return "page pool exhausted";
+    case PDA_ERR_SCRATCH:
+      return "shape needs more device scratch than paged_decode_attn_noalloc holds";
     default: return "unknown status";
   }
 }

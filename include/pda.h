@@ -72,7 +72,9 @@ enum pda_status {
   PDA_ERR_UNSUPPORTED = 2, /* valid but not built: (dtype, dims, page size) */
   PDA_ERR_LAUNCH = 3,      /* the HIP runtime rejected a kernel launch      */
   PDA_ERR_WORKSPACE = 4,   /* workspace smaller than the minimum           */
-  PDA_ERR_POOL_EXHAUSTED = 5 /* fewer free pages than an allocation asks for */
+  PDA_ERR_POOL_EXHAUSTED = 5, /* fewer free pages than an allocation asks for */
+  PDA_ERR_SCRATCH = 6      /* shape needs more than the fixed scratch of
+                              paged_decode_attn_noalloc                     */
 };
 
 enum pda_kv_dtype { PDA_KV_BF16 = 0, PDA_KV_FP8_E4M3 = 1 };
@@ -289,6 +291,38 @@ int paged_decode_attn(const pda_attn_shape* shape, const void* q,
                       int32_t max_seq_len, const int32_t* verdict,
                       void* workspace, size_t workspace_bytes, float* out,
                       void* stream);
+
+/*
+ * paged_decode_attn_noalloc — paged_decode_attn for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments minus the workspace,
+ * the same kernels and results, with the partials in a fixed scratch array
+ * that the library keeps in device memory (one copy per device, 96 MiB,
+ * see paged_decode_attn_noalloc_scratch_bytes, held until the process ends).
+ * The call itself allocates and frees nothing; its first call on a device
+ * looks up that device's copy.
+ *  - Every call on one device shares that device's scratch, and each call
+ *    overwrites it (nothing in it needs to start at zero): calls that may
+ *    overlap on one device (several streams, several host threads) race and
+ *    must be serialised by the caller.
+ *  - PDA_ERR_SCRATCH if the shape cannot run in the scratch even at its
+ *    smallest workspace (vector-ALU path: a header of 4*(num_seqs + 65)
+ *    bytes rounded up to 256 plus num_seqs * Hkv * G*(Dv+2)*4 bytes; latent
+ *    path: num_seqs + 1 partials of Hq*516*4 bytes plus its header). Shapes
+ *    whose full workspace is larger than the scratch run with the split
+ *    chunk widened (vector-ALU) or fewer workgroups (latent), as
+ *    paged_decode_attn does with a small workspace.
+ *  Other arguments, results and errors: as paged_decode_attn.
+ */
+int paged_decode_attn_noalloc(const pda_attn_shape* shape, const void* q,
+                              const void* k_cache, const void* v_cache,
+                              const float* k_scale, const float* v_scale,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              int32_t max_seq_len, const int32_t* verdict,
+                              float* out, void* stream);
+
+/* Bytes of the fixed scratch paged_decode_attn_noalloc runs in. */
+size_t paged_decode_attn_noalloc_scratch_bytes(void);
 
 /* Human-readable name of a status code (static storage). */
 const char* pda_status_string(int status);

@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
                             "pda_hbm_read_probe", "pda_hbm_read_probe_sink_words",
                             "int4_gemv_bf16", "validate_page_tags",
                             "paged_decode_attn_workspace_bytes", "paged_decode_attn",
-                            "pda_status_string"])
+                            "paged_decode_attn_noalloc",
+                            "paged_decode_attn_noalloc_scratch_bytes", "pda_status_string"])
 
 
 def test_library_exports_every_declared_symbol(pda):
@@ -51,6 +52,7 @@ def test_status_strings(pda):
     assert pda.status_string(pda.PDA_ERR_UNSUPPORTED) == "unsupported shape or dtype"
     assert pda.status_string(pda.PDA_ERR_LAUNCH) == "kernel launch failed"
     assert pda.status_string(pda.PDA_ERR_WORKSPACE) == "workspace too small"
+    assert "scratch" in pda.status_string(pda.PDA_ERR_SCRATCH)
     assert pda.status_string(99) == "unknown status"
 
 
@@ -198,3 +200,28 @@ def test_int4_gemv_argument_checks(pda):
     assert g(f, f, ctypes.c_void_p(4097), 1, 16, 128, 128, f, null) == E   # scale odd
     assert g(f, f, f, 1, 16, 128, 128, ctypes.c_void_p(4098), null) == E   # y not 4-aligned
     assert g(f, f, f, 524281, 16, 128, 128, f, null) == U    # too many tokens for the grid
+
+
+def test_noalloc_host_checks(pda):
+    """The allocation-free entry point: its scratch size, and the argument
+    and size checks it makes on the host before touching any device."""
+    lib = pda.load()
+    assert pda.paged_decode_attn_noalloc_scratch_bytes() == 96 << 20
+    fake = ctypes.c_void_p(256)
+    sh = _shape(pda)
+    st = lib.paged_decode_attn_noalloc(ctypes.byref(sh), None, fake, fake, fake, fake, fake,
+                                       fake, 8192, None, fake, None)
+    assert st == pda.PDA_ERR_INVALID_ARG
+    st = lib.paged_decode_attn_noalloc(ctypes.byref(sh), fake, fake, fake, fake, fake, fake,
+                                       fake, -1, None, fake, None)
+    assert st == pda.PDA_ERR_INVALID_ARG
+    # 16384 sequences x 8 kv heads need 545 MB of partials even at one unit
+    # per (sequence, kv head)
+    big = _shape(pda, num_seqs=16384, split_tokens=0)
+    st = lib.paged_decode_attn_noalloc(ctypes.byref(big), fake, fake, fake, fake, fake, fake,
+                                       fake, 8192, None, fake, None)
+    assert st == pda.PDA_ERR_SCRATCH
+    # zero sequences: nothing to do
+    st = lib.paged_decode_attn_noalloc(ctypes.byref(_shape(pda, num_seqs=0)), None, None,
+                                       None, None, None, None, None, 0, None, None, None)
+    assert st == pda.PDA_OK
