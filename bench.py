@@ -14,7 +14,15 @@ Prints one JSON line. `value` is algorithmic KV bytes per step / step time
 timed with HIP events on the launch stream. `cpu_baseline` times the oracle
 on a bounded sample of the same workload on the host cores.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--passes N] [--gpus 1]
+                    [--schedule serial|overlap] [--no-cpu-baseline] [--no-extra]
+
+Every timed figure is the median over N interleaved passes of exactly K
+calls between two HIP events on the launch stream (FP8 and BF16 steps, the
+attention calls alone, and the no-op-tracker step alternate within each
+round), after W warm-up steps. Extra keys: the latent workload's attention
+call against the matrix-core peak, the full-pool workload's step with the
+tag check's share, the BF16 -> FP8 page transcode, the INT4 GEMV.
 """
 from __future__ import annotations
 
@@ -32,6 +40,7 @@ METRIC = ("decode-attn KV GB/s (% HBM peak) + seq-steps/s, FP8 vs BF16 KV, 64×8
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD specification
 MFMA_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 / f16 matrix peak, AMD specification
 WORKLOAD_ID = 3
+DEFAULT_SCHEDULE = "serial"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_64x8k.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_fp8_write_amd", "csrc", "decode_attn.hip")
 
@@ -69,31 +78,47 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def time_steps(db, steps, warmup, torch):
-    """Warm up, then time exactly `steps` whole steps between two HIP events
-    on the launch stream, synchronised on both sides: the step time. A second
-    pass over the same number of steps records an event between the calls of
-    every step and gives the breakdown (kv write, validation, attention) and
-    the attention call's duration; the events between the calls cost time of
-    their own (about 18 us per step here), so the step time comes from the
-    first pass only."""
-    for _ in range(warmup):
-        db.step()
+def median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def timed_pass(fn, steps, torch):
+    """Mean milliseconds of one call of fn over exactly `steps` calls between
+    two HIP events on the current (launch) stream, synchronised on both
+    sides."""
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
     a.record()
     for _ in range(steps):
-        db.step()
+        fn()
     b.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = a.elapsed_time(b) / steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        e = ev[i]
+    return a.elapsed_time(b) / steps
+
+
+def interleaved_passes(fns, steps, passes, torch):
+    """`passes` rounds; each round times every named function once over
+    exactly `steps` calls (timed_pass), in the given order, so that clock
+    and temperature drift reach every function alike. Returns name -> list
+    of per-pass milliseconds per call."""
+    out = {name: [] for name in fns}
+    for _ in range(passes):
+        for name, fn in fns.items():
+            out[name].append(timed_pass(fn, steps, torch))
+    return out
+
+
+def breakdown(db, steps, torch):
+    """One pass with an event between the calls of every step, all on one
+    stream: the mean duration of the kv write, the tag check and the
+    attention call. The events cost time of their own, so the step time
+    never comes from here."""
+    evs = []
+    for _ in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         e[0].record()
         db.write_step()
         e[1].record()
@@ -101,36 +126,13 @@ def time_steps(db, steps, warmup, torch):
         e[2].record()
         db.attend()
         e[3].record()
+        evs.append(e)
     torch.cuda.synchronize()
-    kvw = [e[0].elapsed_time(e[1]) for e in ev]
-    val = [e[1].elapsed_time(e[2]) for e in ev]
-    att = [e[2].elapsed_time(e[3]) for e in ev]
-    step_ev = [e[0].elapsed_time(e[3]) for e in ev]
     mean = lambda xs: sum(xs) / len(xs)
-    q = sorted(att)
-    log(f"step ms: {step_ms:.4f}; attention call ms: min {q[0]:.4f} median {q[len(q) // 2]:.4f} "
-        f"max {q[-1]:.4f}")
-    return dict(wall_ms_per_step=wall * 1e3 / steps, step_ms=step_ms,
-                step_ms_with_call_events=mean(step_ev), kv_write_ms=mean(kvw),
-                validate_ms=mean(val), attn_ms=mean(att), attn_ms_min=min(att),
-                attn_ms_max=max(att))
-
-
-def time_plain_steps(db, steps, warmup, torch, use_verdict):
-    """Step time alone (events around exactly `steps` steps), with the tag
-    check (validate + verdict-gated attention) or without it (no validate
-    call, NULL verdict: the no-op tracker)."""
-    for _ in range(warmup):
-        db.step(use_verdict=use_verdict)
-    torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(steps):
-        db.step(use_verdict=use_verdict)
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / steps
+    return dict(kv_write_ms=mean([e[0].elapsed_time(e[1]) for e in evs]),
+                validate_ms=mean([e[1].elapsed_time(e[2]) for e in evs]),
+                attn_ms_with_events=mean([e[2].elapsed_time(e[3]) for e in evs]),
+                step_ms_with_call_events=mean([e[0].elapsed_time(e[3]) for e in evs]))
 
 
 def pool_cycles(pool, seconds):
@@ -356,47 +358,72 @@ def cpu_baseline(batch, data, host_scales, target_s=12.0):
                       f"attention; {t:.1f} s"}
 
 
-def other_workload(args, torch, np, synth, pda, workload):
-    """One FP8 line for workload 2, 4 (latent, matrix-core path) or 5 (full
-    pool with tag mismatches), timed like the metric's workload."""
-    batch = synth.make_batch(args.workload)
-    cfg = batch.cfg
-    log(f"workload {args.workload}: generating inputs")
-    data = synth.map_seqs(lambda s: batch.kv(s), list(range(batch.B)),
+def gen_data(batch, synth):
+    return synth.map_seqs(lambda s: batch.kv(s), list(range(batch.B)),
                           min(16, os.cpu_count() or 1))
-    db = workload.build(batch, pda.KV_FP8_E4M3, data=data)
+
+
+def latent_leg(args, torch, synth, pda, workload):
+    """The latent workload (64 sequences of U[1024, 32768] tokens, 128 query
+    heads, one 576-dim kv head, per-token scales) on the matrix-core path:
+    the attention call timed like the metric's (median of interleaved
+    passes of exactly K calls), rated against the dense bf16/f16 matrix
+    peak."""
+    batch = synth.make_batch(4)
+    log("latent workload: generating inputs and cache")
+    db = workload.build(batch, pda.KV_FP8_E4M3, data=gen_data(batch, synth))
     db.alloc_workspace()
-    del data
-    r = time_steps(db, args.steps, args.warmup, torch)
-    kv = workload.kv_bytes(batch, pda.KV_FP8_E4M3)
-    attn_s = r["attn_ms"] * 1e-3
-    step_s = r["step_ms"] * 1e-3
+    for _ in range(args.warmup):
+        db.step()
+    t = interleaved_passes({"attn": lambda: db.attend()}, args.steps, args.passes, torch)
+    attn_ms = median(t["attn"])
     flops = workload.attention_flops(batch)
-    line = {
-        "metric": f"decode-attn KV GB/s, FP8 KV, workload {args.workload}",
-        "value": kv / step_s / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": r["step_ms"], "higher_is_better": True,
-        "data": "synthetic",
-        "config": {"workload": cfg.name, "global_batch": batch.B,
-                   "tokens": int(batch.seq_lens.sum())},
-        "attn_ms": r["attn_ms"], "validate_ms": r["validate_ms"],
-        "kv_write_ms": r["kv_write_ms"], "seq_steps_per_s": batch.B / step_s,
-        "kv_GBps_attn": kv / attn_s / 1e9,
-        "verdicts_nonzero": int((db.verdict.cpu().numpy() != 0).sum()),
-    }
-    if cfg.v_in_k:
-        tf = flops / attn_s / 1e12
-        line["roofline"] = {"kernel": "paged_decode_attn latent (partial + combine)",
-                            "bound": "mfma", "achieved": tf, "peak": MFMA_PEAK_TFLOPS,
-                            "unit": "TFLOP/s", "frac": tf / MFMA_PEAK_TFLOPS,
-                            "hbm_frac": kv / attn_s / 1e9 / HBM_PEAK_GBPS,
-                            "algorithmic_flops_per_launch": flops, "traffic": None}
-    else:
-        line["roofline"] = {"kernel": "paged_decode_attn (attn_partial + attn_combine)",
-                            "bound": "hbm", "achieved": kv / attn_s / 1e9,
-                            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                            "frac": kv / attn_s / 1e9 / HBM_PEAK_GBPS, "traffic": None}
-    return line
+    kv = workload.kv_bytes(batch, pda.KV_FP8_E4M3)
+    tf = flops / (attn_ms * 1e-3) / 1e12
+    log(f"latent attention call: {attn_ms:.4f} ms, {tf:.0f} TFLOP/s")
+    out = {"workload": batch.cfg.name, "tokens": int(batch.seq_lens.sum()),
+           "attn_ms": attn_ms, "attn_ms_passes": t["attn"],
+           "roofline": {"kernel": "paged_decode_attn latent (partial + combine)",
+                        "bound": "mfma", "achieved": tf, "peak": MFMA_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": tf / MFMA_PEAK_TFLOPS,
+                        "hbm_frac": kv / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                        "algorithmic_flops_per_launch": flops, "traffic": None}}
+    del db
+    torch.cuda.empty_cache()
+    return out
+
+
+def full_pool_leg(args, torch, synth, pda, workload, overlap):
+    """The full-pool workload (256 lognormal sequences, churned pool, one
+    injected tag mismatch per 10,000 pages, 256 new tokens per step): whole
+    steps with the tag check and with the no-op tracker, interleaved
+    passes; the check's share of the step, and the attention call alone."""
+    batch = synth.make_batch(5)
+    log("full-pool workload: generating inputs and cache")
+    db = workload.build(batch, pda.KV_FP8_E4M3, data=gen_data(batch, synth))
+    db.alloc_workspace()
+    for _ in range(args.warmup):
+        db.step(overlap=overlap)
+    t = interleaved_passes({"on": lambda: db.step(overlap=overlap),
+                            "off": lambda: db.step(use_verdict=False),
+                            "attn": lambda: db.attend()}, args.steps, args.passes, torch)
+    bd = breakdown(db, args.steps, torch)
+    on, off, attn = median(t["on"]), median(t["off"]), median(t["attn"])
+    kv = workload.kv_bytes(batch, pda.KV_FP8_E4M3)
+    log(f"full pool: step {on:.4f} ms (no-op tracker {off:.4f}), attention {attn:.4f} ms")
+    out = {"workload": batch.cfg.name, "tokens": int(batch.seq_lens.sum()),
+           "step_ms": on, "step_ms_no_op_tracker": off, "attn_ms": attn,
+           "tag_check_overhead_frac": on / off - 1.0,
+           "validate_ms": bd["validate_ms"], "validate_frac_of_step":
+               bd["validate_ms"] / bd["step_ms_with_call_events"],
+           "kv_write_ms": bd["kv_write_ms"],
+           "seq_steps_per_s": batch.B / (on * 1e-3),
+           "kv_GBps_step": kv / (on * 1e-3) / 1e9,
+           "pct_hbm_peak_attn": 100.0 * kv / (attn * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+           "verdicts_nonzero": int((db.verdict.cpu().numpy() != 0).sum())}
+    del db
+    torch.cuda.empty_cache()
+    return out
 
 
 def sweep(args, torch, np, synth, pda, workload):
@@ -404,38 +431,43 @@ def sweep(args, torch, np, synth, pda, workload):
     tokens (the 64 x 8192 workload's heads and outliers; automatic split-K,
     which keeps 512-token chunks from 32 sequences up and halves them below
     so that small batches still fill the chip) for B in 1, 8, 16, 32, 64,
-    FP8 and BF16 caches, each timed like the metric's workload; plus cache
-    bytes per token and tokens per GiB of pool."""
+    FP8 and BF16 caches, steps and attention calls timed in interleaved
+    passes; plus cache bytes per token and tokens per GiB of pool."""
     rows = []
     for B in (1, 8, 16, 32, 64):
         batch = synth.make_batch(WORKLOAD_ID, lens=[8192] * B)
-        cfg = batch.cfg
-        data = synth.map_seqs(lambda s: batch.kv(s), list(range(B)),
-                              min(16, os.cpu_count() or 1))
+        data = gen_data(batch, synth)
+        dbs = {}
+        for name, dt in (("fp8", pda.KV_FP8_E4M3), ("bf16", pda.KV_BF16)):
+            dbs[name] = workload.build(batch, dt, data=data)
+            dbs[name].alloc_workspace(split_tokens=0)
+            for _ in range(args.warmup):
+                dbs[name].step()
+        log(f"sweep B={B}")
+        t = interleaved_passes({f"{n}_{w}": (lambda d=d, w=w: d.step() if w == "step"
+                                             else d.attend())
+                                for n, d in dbs.items() for w in ("step", "attn")},
+                               args.steps, args.passes, torch)
         row = {"seqs": B}
         for name, dt in (("fp8", pda.KV_FP8_E4M3), ("bf16", pda.KV_BF16)):
-            db = workload.build(batch, dt, data=data)
-            db.alloc_workspace(split_tokens=0)
-            log(f"sweep B={B} {name}")
-            r = time_steps(db, args.steps, args.warmup, torch)
             kv = workload.kv_bytes(batch, dt)
-            row[name] = {"split": "auto", "step_ms": r["step_ms"], "attn_ms": r["attn_ms"],
-                         "seq_steps_per_s": B / (r["step_ms"] * 1e-3),
-                         "kv_GBps_attn": kv / (r["attn_ms"] * 1e-3) / 1e9,
-                         "pct_hbm_peak_attn": 100.0 * kv / (r["attn_ms"] * 1e-3) / 1e9
+            step, attn = median(t[f"{name}_step"]), median(t[f"{name}_attn"])
+            row[name] = {"split": "auto", "step_ms": step, "attn_ms": attn,
+                         "seq_steps_per_s": B / (step * 1e-3),
+                         "kv_GBps_attn": kv / (attn * 1e-3) / 1e9,
+                         "pct_hbm_peak_attn": 100.0 * kv / (attn * 1e-3) / 1e9
                          / HBM_PEAK_GBPS}
-            del db
-            torch.cuda.empty_cache()
         row["fp8_over_bf16_seq_steps"] = (row["fp8"]["seq_steps_per_s"]
                                           / row["bf16"]["seq_steps_per_s"])
         rows.append(row)
-        del data
+        del dbs, data
+        torch.cuda.empty_cache()
     cfg = synth.CONFIGS[WORKLOAD_ID]
     per_tok = {"fp8": cfg.num_kv_heads * (cfg.head_dim_qk + cfg.head_dim_v),
                "bf16": 2 * cfg.num_kv_heads * (cfg.head_dim_qk + cfg.head_dim_v)}
     return {"metric": "kernel-level concurrency sweep, 8192-token contexts, FP8 vs BF16 KV",
             "unit": "seq-steps/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-            "data": "synthetic", "rows": rows,
+            "passes": args.passes, "data": "synthetic", "rows": rows,
             "capacity": {"cache_bytes_per_token": per_tok,
                          "tokens_per_GiB": {k: (1 << 30) // v for k, v in per_tok.items()}}}
 
@@ -445,11 +477,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--passes", type=int, default=7,
+                    help="timed passes of exactly --steps steps per leg (median reported)")
+    ap.add_argument("--schedule", choices=("serial", "overlap"), default=DEFAULT_SCHEDULE,
+                    help="step schedule: every call on one stream, or the tag check on a "
+                         "second stream beside the kv write (attention waits for both)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-bf16", action="store_true")
-    ap.add_argument("--workload", type=int, default=WORKLOAD_ID, choices=(2, 3, 4, 5),
-                    help="3 (default) is the metric's workload; 2, 4 and 5 print an extra "
-                         "line for the other full-size workloads (4 = latent, matrix cores)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the latent, full-pool, transcode and INT4 legs")
     ap.add_argument("--sweep", action="store_true",
                     help="kernel-level concurrency sweep: 1..64 sequences of 8192 tokens, "
                          "FP8 and BF16; one JSON line")
@@ -485,68 +520,84 @@ def main():
     if args.sweep:
         print(json.dumps(sweep(args, torch, np, synth, pda, workload)), flush=True)
         return
-    if args.workload != WORKLOAD_ID:
-        print(json.dumps(other_workload(args, torch, np, synth, pda, workload)), flush=True)
-        return
-    batch = synth.make_batch(WORKLOAD_ID)
+    overlap = args.schedule == "overlap"
+
+    # page bookkeeping from the library's own pool and tag tracker
+    # (pda_pool_*), checked against the harness pool it replaces
+    batch = synth.make_batch(
+        WORKLOAD_ID, pool_factory=lambda n, o: pda.PagePool(n, initial_order=o))
+    ref_batch = synth.make_batch(WORKLOAD_ID)
+    pool_same = bool(np.array_equal(batch.block_table, ref_batch.block_table)
+                     and np.array_equal(batch.expected_tags, ref_batch.expected_tags)
+                     and np.array_equal(batch.page_tags, ref_batch.page_tags))
+    assert pool_same, "library page pool and harness pool disagree"
+    del ref_batch
     cfg = batch.cfg
+    B = batch.B
     log("generating inputs")
-    data = synth.map_seqs(lambda s: batch.kv(s), list(range(batch.B)), min(16, os.cpu_count() or 1))
-    log("building FP8 cache")
+    data = gen_data(batch, synth)
+    log("building FP8 and BF16 caches")
     fp8 = workload.build(batch, pda.KV_FP8_E4M3, data=data)
     fp8.alloc_workspace()
-    log("timing FP8 steps")
-    r8 = time_steps(fp8, args.steps, args.warmup, torch)
+    bf = workload.build(batch, pda.KV_BF16, data=data)
+    bf.alloc_workspace()
+    for _ in range(args.warmup):
+        fp8.step(overlap=overlap)
+        bf.step(overlap=overlap)
+    log(f"timing {args.passes} interleaved passes of {args.steps} steps ({args.schedule})")
+    t = interleaved_passes({
+        "fp8_step": lambda: fp8.step(overlap=overlap),
+        "bf16_step": lambda: bf.step(overlap=overlap),
+        "fp8_attn": lambda: fp8.attend(),
+        "bf16_attn": lambda: bf.attend(),
+        "fp8_step_no_op_tracker": lambda: fp8.step(use_verdict=False),
+        "fp8_step_other_schedule": lambda: fp8.step(overlap=not overlap),
+        "bf16_step_other_schedule": lambda: bf.step(overlap=not overlap),
+    }, args.steps, args.passes, torch)
+    med = {k: median(v) for k, v in t.items()}
+    for k, v in med.items():
+        log(f"  {k}: {v:.4f} ms (passes {', '.join(f'{x:.4f}' for x in t[k])})")
+    bd8 = breakdown(fp8, args.steps, torch)
+    bd16 = breakdown(bf, args.steps, torch)
     kv8 = workload.kv_bytes(batch, pda.KV_FP8_E4M3)
-    B = batch.B
-    ceiling = read_ceiling(torch, pda)
-    # tag-check overhead: the same steps with the no-op tracker, interleaved
-    # on/off passes so clock drift cancels
-    log("timing steps with and without the tag check")
-    on, off = [], []
-    for _ in range(3):
-        off.append(time_plain_steps(fp8, args.steps, 10, torch, use_verdict=False))
-        on.append(time_plain_steps(fp8, args.steps, 10, torch, use_verdict=True))
-    tracker = {"step_ms_check_on": min(on), "step_ms_check_off": min(off),
-               "overhead_frac": min(on) / min(off) - 1.0}
-    res_bf16 = None
-    if not args.no_bf16:
-        log("building BF16 cache")
-        bf = workload.build(batch, pda.KV_BF16, data=data)
-        bf.alloc_workspace()
-        log("timing BF16 steps")
-        r16 = time_steps(bf, args.steps, args.warmup, torch)
-        kv16 = workload.kv_bytes(batch, pda.KV_BF16)
-        res_bf16 = {
-            "kv_GBps_step": kv16 / (r16["step_ms"] * 1e-3) / 1e9,
-            "kv_GBps_attn": kv16 / (r16["attn_ms"] * 1e-3) / 1e9,
-            "seq_steps_per_s": B / (r16["step_ms"] * 1e-3),
-            "step_ms": r16["step_ms"], "attn_ms": r16["attn_ms"],
-            "validate_ms": r16["validate_ms"], "kv_write_ms": r16["kv_write_ms"]}
-        log("timing the BF16 -> FP8 page transcode of the whole pool")
-        res_bf16["transcode"] = time_transcode(bf, fp8, args, torch, np, pda)
-        del bf
-        torch.cuda.empty_cache()
-    log("timing the INT4 weight-only GEMV")
-    int4 = time_int4(torch, pda)
-
-    step_s = r8["step_ms"] * 1e-3
-    attn_s = r8["attn_ms"] * 1e-3
+    kv16 = workload.kv_bytes(batch, pda.KV_BF16)
+    step8, step16 = med["fp8_step"], med["bf16_step"]
+    attn8, attn16 = med["fp8_attn"], med["bf16_attn"]
     # algorithmic bytes of one attention call: KV, q, out, block-table entries
     q_bytes = B * cfg.num_q_heads * cfg.head_dim_qk * 2
     out_bytes = B * cfg.num_q_heads * cfg.head_dim_v * 4
     bt_bytes = int(np.sum(-(-batch.seq_lens // cfg.page_size))) * 4
     attn_bytes = kv8 + q_bytes + out_bytes + bt_bytes
-    achieved = attn_bytes / attn_s / 1e9
-    seq_steps = B / step_s
+    achieved = attn_bytes / (attn8 * 1e-3) / 1e9
+    seq_steps = B / (step8 * 1e-3)
+    seq_steps16 = B / (step16 * 1e-3)
+    res_bf16 = {"step_ms": step16, "attn_ms": attn16, "seq_steps_per_s": seq_steps16,
+                "kv_GBps_step": kv16 / (step16 * 1e-3) / 1e9,
+                "kv_GBps_attn": kv16 / (attn16 * 1e-3) / 1e9,
+                "step_ms_passes": t["bf16_step"], "attn_ms_passes": t["bf16_attn"],
+                "step_ms_other_schedule": med["bf16_step_other_schedule"],
+                "validate_ms": bd16["validate_ms"], "kv_write_ms": bd16["kv_write_ms"]}
+    ceiling = read_ceiling(torch, pda)
+    extra = {}
+    if not args.no_extra:
+        log("timing the BF16 -> FP8 page transcode of the whole pool")
+        res_bf16["transcode"] = time_transcode(bf, fp8, args, torch, np, pda)
+    del bf
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        extra["latent_workload"] = latent_leg(args, torch, synth, pda, workload)
+        extra["full_pool_workload"] = full_pool_leg(args, torch, synth, pda, workload, overlap)
+        log("timing the INT4 weight-only GEMV")
+        extra["int4_gemv"] = time_int4(torch, pda)
+
     line = {
         "metric": METRIC,
-        "value": kv8 / step_s / 1e9,
+        "value": kv8 / (step8 * 1e-3) / 1e9,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": r8["step_ms"],
+        "ms_per_step": step8,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -558,32 +609,41 @@ def main():
                                "validation + attention",
                    "global_batch": B, "seq_len": int(batch.seq_lens[0]),
                    "parallelism": "single GPU"},
-        "pct_hbm_peak_step": 100.0 * kv8 / step_s / 1e9 / HBM_PEAK_GBPS,
+        "timing": f"median of {args.passes} interleaved passes of exactly {args.steps} "
+                  f"steps (FP8, BF16 and the other legs alternate) after {args.warmup} "
+                  f"warm-up steps of each",
+        "schedule": args.schedule,
+        "pct_hbm_peak_step": 100.0 * kv8 / (step8 * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "seq_steps_per_s": seq_steps,
         "tokens_per_s": seq_steps,
-        "attn_ms": r8["attn_ms"],
-        "validate_ms": r8["validate_ms"],
-        "kv_write_ms": r8["kv_write_ms"],
-        "validate_frac_of_step": r8["validate_ms"] / r8["step_ms_with_call_events"],
-        "tag_check": tracker,
+        "step_ms_passes": t["fp8_step"],
+        "step_ms_other_schedule": med["fp8_step_other_schedule"],
+        "attn_ms": attn8,
+        "attn_ms_passes": t["fp8_attn"],
+        "validate_ms": bd8["validate_ms"],
+        "kv_write_ms": bd8["kv_write_ms"],
+        "validate_frac_of_step": bd8["validate_ms"] / bd8["step_ms_with_call_events"],
+        "step_ms_with_call_events": bd8["step_ms_with_call_events"],
+        "tag_check": {"step_ms_check_on": step8,
+                      "step_ms_check_off": med["fp8_step_no_op_tracker"],
+                      "overhead_frac": step8 / med["fp8_step_no_op_tracker"] - 1.0,
+                      "tags_from": "libpda.so page pool (pda_pool_*), identical to the "
+                                   "harness pool's bookkeeping"},
         "page_pool": time_page_pool(pda, np),
         "hbm_read_ceiling": ceiling,
-        "int4_gemv": int4,
-        "step_ms_with_call_events": r8["step_ms_with_call_events"],
-        "kv_GBps_attn": kv8 / attn_s / 1e9,
-        "wall_ms_per_step": r8["wall_ms_per_step"],
+        "kv_GBps_attn": kv8 / (attn8 * 1e-3) / 1e9,
+        "fp8_over_bf16_seq_steps": seq_steps / seq_steps16,
+        "fp8_over_bf16_attn": attn16 / attn8,
+        "bf16": res_bf16,
         "roofline": {"kernel": "paged_decode_attn (attn_partial + attn_combine)",
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "algorithmic_bytes_per_launch": attn_bytes,
-                     "frac_of_measured_random_2KB_ceiling":
-                         achieved / ceiling["random_2KB_GBps"],
+                     "frac_of_measured_read_ceiling":
+                         achieved / max(ceiling.values()),
                      "traffic": measured_traffic()},
     }
-    if res_bf16 is not None:
-        line["bf16"] = res_bf16
-        line["fp8_over_bf16_seq_steps"] = seq_steps / res_bf16["seq_steps_per_s"]
-        line["fp8_over_bf16_attn"] = res_bf16["attn_ms"] / r8["attn_ms"]
+    line.update(extra)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
         line["cpu_baseline"] = cpu_baseline(batch, data, fp8.host_scales)

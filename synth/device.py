@@ -47,6 +47,9 @@ class DeviceBatch:
     host_scales: tuple = field(default=(None, None))
     workspace: object = None
     shape: object = None
+    _side: object = None
+    _fork: object = None
+    _join: object = None
 
     @property
     def cfg(self):
@@ -112,11 +115,31 @@ class DeviceBatch:
                           self.verdict if use_verdict else None, self.workspace, self.out,
                           stream=stream)
 
-    def step(self, use_verdict: bool = True, stream=None):
-        self.write_step(stream)
-        if use_verdict:
-            self.validate(stream)
-        self.attend(use_verdict, stream)
+    def step(self, use_verdict: bool = True, stream=None, overlap: bool = False):
+        """One decode step: kv write of the newest tokens, the tag check,
+        attention. overlap: the tag check runs on a second stream (default
+        priority) beside the kv write, which it does not depend on; attention
+        waits for both."""
+        if not (overlap and use_verdict):
+            self.write_step(stream)
+            if use_verdict:
+                self.validate(stream)
+            self.attend(use_verdict, stream)
+            return
+        import torch
+        main = torch.cuda.current_stream() if stream is None else stream
+        if self._side is None:
+            self._side = torch.cuda.Stream(device=self.q.device)
+            self._fork = torch.cuda.Event()
+            self._join = torch.cuda.Event()
+        # the check rewrites the verdicts the previous step's attention read
+        self._fork.record(main)
+        self._side.wait_event(self._fork)
+        self.validate(self._side)
+        self._join.record(self._side)
+        self.write_step(main)
+        main.wait_event(self._join)
+        self.attend(True, main)
 
 
 def build(batch: synth.Batch, kv_dtype: int, *, device: str = "cuda", data=None,
