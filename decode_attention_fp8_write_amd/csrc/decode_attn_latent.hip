@@ -75,9 +75,13 @@ constexpr int kMaxSeqsL = 2048;
 // Q of k-steps [0, kQReg) stays in registers, the rest is read from LDS
 // (registers would spill otherwise; a spill reload waits on the memory
 // counter that also tracks the page copy in flight)
-constexpr int kQReg = 9;
-constexpr int kQLdsTile = (kKSteps - kQReg) * 64 * 16;   // bytes per 16-head tile
-constexpr int kMaxTilesL = 8;                             // 128 heads
+constexpr int kQReg = 11;
+constexpr int kQLdsWave = (kKSteps - kQReg) * 64 * 16;   // bytes per wave (16 heads)
+constexpr int kMaxHeadsL = 16 * kMaxWavesL;               // 128
+// The page's weights p (f16) for the PV product, one row of 64 tokens per
+// head, rows padded to 144 bytes so that the 16 rows one 16-byte operand read
+// touches start in 16 different bank quads.
+constexpr int kPRow = 144;
 
 template <int F, int L>
 struct sfor {
@@ -131,57 +135,121 @@ struct PageBuf {
   float sraw[kS];  // the page's scales as stored (copied with the codes)
 };
 
-// acc *= alpha for the (rare) running-max move, through global memory:
-// store the accumulators (the lane's head rows, layout of the partial),
-// wait, and load them back scaled, one tile at a time (the scheduling
-// barriers keep the compiler from hoisting every load, whose registers
-// would push values out to scratch). The register reloads the compiler
-// still leaves pending at the end of this branch make the first PV product
-// of every page wait for the page copy in flight; measured, that costs less
-// than issuing the copy after this point.
-// acc[c][ht] register r: dim 16c + 4g + r of head tile ht, column n.
-constexpr int kRescaleTiles = 1;
-template <int HT>
-__device__ __forceinline__ void rescale_via(float* const (&row)[HT], f32x4_t (&acc)[kDTiles][HT],
-                                            const float (&alpha)[HT]) {
-  const int g = __lane_id() >> 4;
-#pragma unroll
-  for (int c = 0; c < kDTiles; ++c)
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
-      *reinterpret_cast<f32x4_t*>(row[ht] + 16 * c + 4 * g) = acc[c][ht];
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  sfor<0, kDTiles / kRescaleTiles>::run([&](auto C4) {
-    constexpr int c0 = kRescaleTiles * decltype(C4)::value;
-#pragma unroll
-    for (int c = c0; c < c0 + kRescaleTiles; ++c)
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
-        acc[c][ht] = *reinterpret_cast<const f32x4_t*>(row[ht] + 16 * c + 4 * g) * alpha[ht];
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_sched_barrier(0);
+// The PV product is split by value dims over the workgroup's eight waves:
+// wave w owns the four 16-dim column groups 4w .. 4w+3 (dims 64w .. +63).
+constexpr int kPvGroups = kDTiles / kMaxWavesL;
+
+// acc *= alpha for the (rare) running-max move, through this fragment's
+// partial slot in global memory (written again at the end): the
+// accumulators are stored straight from the matrix-core registers, scaled
+// there, and loaded straight back, all in inline asm addressed by one
+// per-lane 32-bit offset, a wave-uniform base per head tile and immediate
+// offsets per column group. Nothing here takes more than a handful of
+// vector registers, so the rare branch does not push the rest of the
+// kernel's registers out to scratch (copying the accumulators through
+// vector registers, or keeping a 64-bit address per tile, did). Every asm
+// statement that loads waits for its own loads.
+// acc[c][ht] register r: dim 16(cg0 + c) + 4g + r of head 16 ht + n, at
+// byte 4((16 ht + n) kRow + 16(cg0 + c) + 4g + r) of the slot.
+template <int C, int HT, int NH>
+__device__ __forceinline__ void rescale_store(uint32_t voff, const float* b,
+                                              const f32x4_t (&acc)[kPvGroups][NH]) {
+  asm volatile("global_store_dwordx4 %0, %1, %2 offset:%3"
+               :: "v"(voff), "a"(acc[C][HT]), "s"(b), "n"(64 * C) : "memory");
+}
+template <int C>
+__device__ __forceinline__ void rescale_scale(uint32_t voff, const float* b, float al) {
+  float t0, t1, t2, t3;
+  asm volatile(
+      "global_load_dword %0, %4, %5 offset:%6\n\t"
+      "global_load_dword %1, %4, %5 offset:%7\n\t"
+      "global_load_dword %2, %4, %5 offset:%8\n\t"
+      "global_load_dword %3, %4, %5 offset:%9\n\t"
+      "s_waitcnt vmcnt(0)\n\t"
+      "v_mul_f32 %0, %0, %10\n\t"
+      "v_mul_f32 %1, %1, %10\n\t"
+      "v_mul_f32 %2, %2, %10\n\t"
+      "v_mul_f32 %3, %3, %10\n\t"
+      "s_nop 1\n\t"
+      "global_store_dword %4, %0, %5 offset:%6\n\t"
+      "global_store_dword %4, %1, %5 offset:%7\n\t"
+      "global_store_dword %4, %2, %5 offset:%8\n\t"
+      "global_store_dword %4, %3, %5 offset:%9"
+      : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+      : "v"(voff), "s"(b), "n"(64 * C), "n"(64 * C + 4), "n"(64 * C + 8), "n"(64 * C + 12),
+        "v"(al)
+      : "memory");
+}
+template <int C, int HT, int NH>
+__device__ __forceinline__ void rescale_load(uint32_t voff, const float* b,
+                                             f32x4_t (&acc)[kPvGroups][NH]) {
+  asm volatile("global_load_dwordx4 %0, %1, %2 offset:%3\n\ts_waitcnt vmcnt(0)"
+               : "=a"(acc[C][HT]) : "v"(voff), "s"(b), "n"(64 * C) : "memory");
+}
+
+template <int NH>
+__device__ __forceinline__ void rescale_via(const float* slot, f32x4_t (&acc)[kPvGroups][NH],
+                                            const float* alpha_lds, int cg0) {
+  constexpr int CG = kPvGroups;
+  const int lane = __lane_id();
+  const int g = lane >> 4, n = lane & 15;
+  const uint32_t voff = (uint32_t)((n * kRow + 16 * cg0 + 4 * g) * 4);
+  // wave-uniform base of head tile ht (scalar registers)
+  auto base = [&](int ht) -> const float* {
+    const uint64_t b = (uint64_t)(uintptr_t)(slot + (int64_t)16 * ht * kRow);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    return (const float*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  };
+  sfor<0, NH * CG>::run([&](auto I) {
+    constexpr int ht = decltype(I)::value / CG, c = decltype(I)::value % CG;
+    rescale_store<c, ht, NH>(voff, base(ht), acc);
+  });
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // scale in place: one tile's four dwords per statement (the loads are
+  // waited for inside it; two wait states between the multiplies and the
+  // stores that read their results)
+  sfor<0, NH * CG>::run([&](auto I) {
+    constexpr int ht = decltype(I)::value / CG, c = decltype(I)::value % CG;
+    rescale_scale<c>(voff, base(ht), alpha_lds[16 * ht + n]);
+  });
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  sfor<0, NH * CG>::run([&](auto I) {
+    constexpr int ht = decltype(I)::value / CG, c = decltype(I)::value % CG;
+    rescale_load<c, ht, NH>(voff, base(ht), acc);
   });
 }
 
-// NW waves of HT 16-head tiles each (NW * HT * 16 query heads). With one
-// tile per wave the eight waves of 128 heads run two to a SIMD, so one
-// wave's softmax and conversions overlap the other's matrix products.
-template <int NW, int HT>
-__global__ __launch_bounds__(64 * NW)
-__attribute__((amdgpu_waves_per_eu(HT == 1 ? 2 : 1, HT == 1 ? 2 : 1)))
+// Eight waves for NH 16-head tiles (16 NH query heads). QK is split by
+// heads: wave w < NH multiplies the page's keys with the Q of heads
+// [16w, 16w+16) and takes their softmax (waves past NH have no QK work). PV
+// is split by value dims: wave w owns column groups 4w .. 4w+3 of the output
+// for every head, reading all heads' weights from LDS, so each V code is
+// converted once per workgroup. Two waves run per SIMD, so one wave's
+// conversions and softmax overlap the other's matrix products.
+template <int NH>
+__global__ __launch_bounds__(64 * kMaxWavesL)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
 void latent_partial_kernel(LatArgs a) {
+  constexpr int NW = kMaxWavesL;
+  constexpr int CG = kPvGroups;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  PageBuf* buf = reinterpret_cast<PageBuf*>(smem);                 // [2]
-  uint8_t* qlds_all = smem + 2 * sizeof(PageBuf);                  // kMaxTilesL x kQLdsTile
-  int* tmp = reinterpret_cast<int*>(qlds_all + kMaxTilesL * kQLdsTile);  // kMaxThreadsL + 1
-  int* pref = tmp + kMaxThreadsL + 1;                               // B + 1
+  PageBuf* buf = reinterpret_cast<PageBuf*>(smem);                    // [2]
+  uint8_t* qlds_all = smem + 2 * sizeof(PageBuf);                     // NW x kQLdsWave
+  uint8_t* pbuf = qlds_all + kMaxWavesL * kQLdsWave;                  // [Hq][kPRow]
+  float* alpha_s = reinterpret_cast<float*>(pbuf + kMaxHeadsL * kPRow);  // [Hq]
+  int* flag_s = reinterpret_cast<int*>(alpha_s + kMaxHeadsL);          // [NH]
+  int* tmp = flag_s + kMaxWavesL;                                      // kMaxThreadsL + 1
+  int* pref = tmp + kMaxThreadsL + 1;                                  // B + 1
   constexpr int NT = 64 * NW;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int g = lane >> 4;        // 16-lane group: MFMA k slice / output row quad
   const int n = lane & 15;        // MFMA row (A) or column (B, output)
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int cg0 = CG * wv;        // first PV column group of this wave
+  const bool qk = wv < NH;        // this wave has QK heads (wave-uniform)
 
   const int T = [&] {
     const int per = (a.B + NT - 1) / NT;
@@ -224,7 +292,7 @@ void latent_partial_kernel(LatArgs a) {
   const int lo = (int)((long long)w * T / W);
   const int hi = (int)((long long)(w + 1) * T / W);
   const float c0 = a.sm_scale * kLog2eL;
-  const int head0 = wave * 16 * HT;
+  const int head0 = wave * 16;    // this wave's QK heads
 
   int gp = lo;
   while (gp < hi) {
@@ -239,44 +307,37 @@ void latent_partial_kernel(LatArgs a) {
     const int j1 = min(hi, pref[s + 1]) - pref[s];
     const int len = a.lens[s];
     const int32_t* btrow = a.bt + (int64_t)s * a.max_blocks;
-    float* prow[HT];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
-      prow[ht] = a.part + ((int64_t)(w + s) * a.Hq + head0 + 16 * ht + n) * kRow;
+    // this fragment's partial slot; the PV output rows this lane holds are
+    // those of heads 16 ht + n
+    float* const slot = a.part + (int64_t)(w + s) * a.Hq * kRow;
+    float* const prow = slot + n * kRow;
 
     // ---- Q of this wave's heads, resident for the fragment --------------
-    // B operand of k-step k, head tile ht: lane (head 16 ht + n, group g)
-    // holds dims 32k + 8g .. +7. Steps below kQReg stay in registers; the
-    // others go to this wave's LDS region as [k - kQReg][ht][lane][16 bytes]
-    // (only this wave reads it, after its own writes).
-    bf16x8_t qreg[HT][kQReg];
-    uint8_t* qlds = qlds_all + wave * HT * kQLdsTile + lane * 16;
-    {
+    // B operand of k-step k: lane (head head0 + n, group g) holds dims
+    // 32k + 8g .. +7. Steps below kQReg stay in registers; the others go to
+    // this wave's LDS region as [k - kQReg][lane][16 bytes] (only this wave
+    // reads it, after its own writes).
+    bf16x8_t qreg[kQReg];
+    uint8_t* qlds = qlds_all + wave * kQLdsWave + lane * 16;
+    if (qk) {
       const uint16_t* qrow = a.q + ((int64_t)s * a.Hq + head0 + n) * kDk + 8 * g;
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-        for (int k = 0; k < kKSteps; ++k) {
-          const uint4 v = *reinterpret_cast<const uint4*>(qrow + 16 * ht * kDk + 32 * k);
-          if (k < kQReg)
-            qreg[ht][k] = __builtin_bit_cast(bf16x8_t, v);
-          else
-            *reinterpret_cast<uint4*>(qlds + ((k - kQReg) * HT + ht) * 1024) = v;
-        }
+      for (int k = 0; k < kKSteps; ++k) {
+        const uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * k);
+        if (k < kQReg)
+          qreg[k] = __builtin_bit_cast(bf16x8_t, v);
+        else
+          *reinterpret_cast<uint4*>(qlds + (k - kQReg) * 1024) = v;
+      }
     }
 
-    f32x4_t acc[kDTiles][HT];
+    f32x4_t acc[CG][NH];
 #pragma unroll
-    for (int c = 0; c < kDTiles; ++c)
+    for (int c = 0; c < CG; ++c)
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht) acc[c][ht] = f32x4_t{};
-    // running max of y per head tile (the same in the four lanes of a head)
-    float m[HT], l[HT];   // l: this lane's tokens' share of the weight sum
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      m[ht] = -INFINITY;
-      l[ht] = 0.0f;
-    }
+      for (int ht = 0; ht < NH; ++ht) acc[c][ht] = f32x4_t{};
+    // running max of y of this lane's QK head (the same in its four lanes)
+    float m = -INFINITY, l = 0.0f;   // l: this lane's tokens' share of the weight sum
     bool bad = false;
 
     // ---- page staging ------------------------------------------------------
@@ -300,14 +361,12 @@ void latent_partial_kernel(LatArgs a) {
           (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)pb.codes));
       // The page base is wave-uniform: each copy takes an SGPR base (page +
       // i KB, scalar arithmetic) and the one per-lane offset lane * 16, so no
-      // per-copy lane address is kept in (or spilled from) vector registers;
-      // a spilled one would be reloaded, and waited for, before every copy.
+      // per-copy lane address is kept in (or spilled from) vector registers.
       // (readfirstlane takes and returns 32 bits: each half separately)
       const uint64_t s64 = (uint64_t)(uintptr_t)src;
       const uint32_t s_lo = __builtin_amdgcn_readfirstlane((uint32_t)s64);
       const uint32_t s_hi = __builtin_amdgcn_readfirstlane((uint32_t)(s64 >> 32));
       const uint8_t* srcu = (const uint8_t*)(uintptr_t)(((uint64_t)s_hi << 32) | s_lo);
-      const int wv = __builtin_amdgcn_readfirstlane(wave);
       // recomputed here (opaque to the compiler, three VALU instructions)
       // rather than kept live across the page and spilled
       uint32_t lane16;
@@ -358,37 +417,37 @@ void latent_partial_kernel(LatArgs a) {
     fetch(j0, buf[0]);
     for (int j = j0; j < j1; ++j) {
       PageBuf& pb = buf[(j - j0) & 1];
-      // page j's copy (and every earlier load) complete, then publish
+      // page j's copy (and every earlier load) complete, then publish; past
+      // this barrier every wave has also finished the PV product of page j-1,
+      // so the weights buffer and the rescale factors may be rewritten
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       // Page j's per-token arrays first, then the next page's copy (the other
       // buffer's last readers, page j - 1, passed the barrier above). Nothing
       // after the copy waits on the vector memory counter until the top of
-      // the next page: a wait there (a register reload, a scale load) would
-      // wait for the whole copy and serialise it with this page's products.
+      // the next page, except the rare rescale: a wait there would wait for
+      // the whole copy and serialise it with this page's products.
       finish(j, pb);
       if (j + 1 < j1) fetch(j + 1, buf[(j + 1 - j0) & 1]);
       __syncthreads();
 
-      // ---- QK: S^T (64 tokens x 16 HT heads) as 4 x HT tiles of 16 x 16 --
+      if (qk) {
+      // ---- QK: S^T (64 tokens x 16 heads) as 4 tiles of 16 x 16 ----------
       // A operand of k-step k, token tile t: lane (row i = n, group g) holds
-      // the codes of dims 32k + 8g .. +7 of the tile's row-i token (column
-      // group 2k + g/2, bytes 8(g&1) .. +7 of its 16-byte slot; one 8-byte LDS
+      // the codes of dims 32k + 8g .. +7 of token 16t + n (column group
+      // 2k + g/2, bytes 8(g&1) .. +7 of its 16-byte slot; one 8-byte LDS
       // read). Unit u = 4k + t; reads run four units ahead, and the
       // scheduling barrier per unit keeps the compiler from hoisting every
-      // read and conversion (a register each).
-      f32x4_t st[4][HT];
+      // read and conversion (a register each). A half-wave reads 16 tokens'
+      // whole slots: every bank once.
+      f32x4_t st[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) st[t][ht] = f32x4_t{};
+      for (int t = 0; t < 4; ++t) st[t] = f32x4_t{};
       {
-        const uint8_t* rowe = pb.codes + (g >> 1) * (kS * 16) + n * 16 + 8 * (g & 1);
-        const uint8_t* rowo = pb.codes + (g >> 1) * (kS * 16) + (n ^ 8) * 16 + 8 * (g & 1);
+        const uint8_t* rowk = pb.codes + (g >> 1) * (kS * 16) + n * 16 + 8 * (g & 1);
         auto rdk = [&](int u) -> uint2 {
           const int k = u >> 2, t = u & 3;
-          return *reinterpret_cast<const uint2*>((t & 1 ? rowo : rowe) + k * (2 * kS * 16) +
-                                                 t * (16 * 16));
+          return *reinterpret_cast<const uint2*>(rowk + k * (2 * kS * 16) + t * (16 * 16));
         };
         constexpr int kAhead = 4;
         constexpr int kUnits = 4 * kKSteps;
@@ -396,11 +455,11 @@ void latent_partial_kernel(LatArgs a) {
 #pragma unroll
         for (int u = 0; u < kAhead; ++u) ring[u] = rdk(u);
         // LDS-resident Q of step k is read during step k - 1 (unit t = 1)
-        auto rdq = [&](int k, int ht) -> bf16x8_t {
-          return __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const uint4*>(qlds + ((k - kQReg) * HT + ht) * 1024));
+        auto rdq = [&](int k) -> bf16x8_t {
+          return __builtin_bit_cast(bf16x8_t,
+                                    *reinterpret_cast<const uint4*>(qlds + (k - kQReg) * 1024));
         };
-        bf16x8_t qn[2][HT];
+        bf16x8_t qn[2];
         sfor<0, kUnits>::run([&](auto U) {
           constexpr int u = decltype(U)::value;
           constexpr int k = u >> 2, t = u & 3;
@@ -410,136 +469,124 @@ void latent_partial_kernel(LatArgs a) {
           const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw.y, 1.0f, false);
           const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw.y, 1.0f, true);
           if constexpr (u + kAhead < kUnits) ring[u % kAhead] = rdk(u + kAhead);
-          if constexpr (t == 1 && k + 1 >= kQReg && k + 1 < kKSteps) {
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) qn[(k + 1) & 1][ht] = rdq(k + 1, ht);
-          }
+          if constexpr (t == 1 && k + 1 >= kQReg && k + 1 < kKSteps) qn[(k + 1) & 1] = rdq(k + 1);
           const bf16x8_t av = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht) {
-            if constexpr (k < kQReg)
-              st[t][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[ht][k], st[t][ht], 0, 0, 0);
-            else
-              st[t][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qn[k & 1][ht], st[t][ht], 0, 0, 0);
-          }
+          if constexpr (k < kQReg)
+            st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[k], st[t], 0, 0, 0);
+          else
+            st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qn[k & 1], st[t], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         });
       }
 
-      // ---- softmax (log2 units, scale folded in) --------------------------
-      // st[t][ht] register r holds token 16t + 4(g ^ 2(t&1)) + r of head
-      // 16 ht + n (row 4g + r of the tile)
-      float bm[HT];
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) bm[ht] = -INFINITY;
+      // ---- softmax of this wave's heads (log2 units, scale folded in) -----
+      // st[t] register r holds token 16t + 4g + r of head head0 + n
+      float bm = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int t0 = 16 * t + 4 * (g ^ (2 * (t & 1)));
+        const int t0 = 16 * t + 4 * g;
         const float4 av = *reinterpret_cast<const float4*>(pb.a + t0);
         const float4 bv = *reinterpret_cast<const float4*>(pb.b + t0);
         const float aa[4] = {av.x, av.y, av.z, av.w};
         const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht) {
-            const float v = fmaf(st[t][ht][r], aa[r], bb[r]);
-            st[t][ht][r] = v;
-            bm[ht] = fmaxf(bm[ht], v);
-          }
-      }
-      bool mv[HT];
-      bool any_mv = false;
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        bm[ht] = fmaxf(bm[ht], shfl_xor_f32(bm[ht], 16));
-        bm[ht] = fmaxf(bm[ht], shfl_xor_f32(bm[ht], 32));
-        mv[ht] = bm[ht] > m[ht] + kTauL;
-        any_mv |= mv[ht];
-      }
-      if (__ballot(any_mv) != 0) {
-        // some head's max moved by more than the threshold: rescale those
-        float mn[HT], al[HT];
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-          mn[ht] = mv[ht] ? bm[ht] : m[ht];
-          al[ht] = mv[ht] ? __builtin_amdgcn_exp2f(m[ht] - mn[ht]) : 1.0f;
+        for (int r = 0; r < 4; ++r) {
+          const float v = fmaf(st[t][r], aa[r], bb[r]);
+          st[t][r] = v;
+          bm = fmaxf(bm, v);
         }
-        if (m[0] != -INFINITY) {   // uniform: every head has a finite max after page 1
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht) l[ht] *= al[ht];
-          // acc *= alpha, as a round trip through this fragment's partial
-          // slot (written again at the end): multiplying the accumulators in
-          // place would pull all of them out of the matrix-core registers
-          rescale_via<HT>(prow, acc, al);
-        }
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) m[ht] = mn[ht];
       }
-      // p' = 2^(y - m), packed to f16 as the B operand of PV: k-step kk, head
-      // tile ht takes registers 0..3 of token tiles 2kk and 2kk+1
-      f16x8_t pk[2][HT];
+      bm = fmaxf(bm, shfl_xor_f32(bm, 16));
+      bm = fmaxf(bm, shfl_xor_f32(bm, 32));
+      // the running max moves only when the page's max exceeds it by more
+      // than the threshold; alpha rescales what was summed under the old max
+      const bool mv = bm > m + kTauL;
+      const float m_old = m;
+      if (mv) m = bm;
+      const float al = mv ? __builtin_amdgcn_exp2f(m_old - m) : 1.0f;
+      l *= al;
+      const bool resc = __ballot(mv && m_old != -INFINITY) != 0;
+      if (g == 0) alpha_s[head0 + n] = al;
+      if (lane == 0) flag_s[wave] = resc ? 1 : 0;
+      // p' = 2^(y - m) as f16, to this head's row of the weights buffer:
+      // lane (n, g) holds tokens 16t + 4g .. +3, one 8-byte store per tile
+      uint8_t* prow_p = pbuf + (head0 + n) * kPRow + 8 * g;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int t0 = 16 * t + 4 * (g ^ (2 * (t & 1)));
+        const int t0 = 16 * t + 4 * g;
         const float4 iv = *reinterpret_cast<const float4*>(pb.inv + t0);
         const float ii[4] = {iv.x, iv.y, iv.z, iv.w};
+        _Float16 ph[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht) {
-            const float p = __builtin_amdgcn_exp2f(st[t][ht][r] - m[ht]);
-            l[ht] = fmaf(p, ii[r], l[ht]);
-            pk[t >> 1][ht][4 * (t & 1) + r] = (_Float16)p;
-          }
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(st[t][r] - m);
+          l = fmaf(p, ii[r], l);
+          ph[r] = (_Float16)p;
+        }
+        *reinterpret_cast<uint2*>(prow_p + 32 * t) = __builtin_bit_cast(uint2, ph);
       }
+      }
+      __syncthreads();
 
-      // ---- PV: O^T (512 dims x 16 HT heads) += V^T P^T ---------------------
-      // k-step kk, 16-lane group g: row b of the transpose read is the token
-      // whose p sits in element b of the group's B operand: 32kk + 4g + b
-      // (b < 4, tile 2kk) or 32kk + 16 + 4(g ^ 2) + b - 4 (b >= 4, tile
-      // 2kk+1). Lane 2b + e supplies that token's bytes 8e .. 8e+7 of
-      // column group c (dims 16c .. 16c+15); lane i receives dim 16c + i.
+      // ---- PV: O^T (this wave's dims x all heads) += V^T P^T ---------------
+      // Heads whose running max moved: acc *= alpha first (rare).
+      {
+        int fl = 0;
+#pragma unroll
+        for (int i = 0; i < NH; ++i) fl |= flag_s[i];
+        if (fl != 0) rescale_via<NH>(slot, acc, alpha_s, cg0);
+      }
+      // k-step kk covers tokens 32kk .. +31. A operand (V^T, column group
+      // cg0 + c): the transpose read ds_read_b64_tr_b8, lane 2b + e of each
+      // 16-lane group g addressing token 32kk + 8g + b, bytes 8e .. +7 of
+      // the group's 16-byte slot, leaves in lane i the codes of dim
+      // 16(cg0 + c) + i for tokens 32kk + 8g .. +7 (element b = token
+      // 32kk + 8g + b). B operand (P^T, head tile ht): lane (n, g) reads
+      // the weights of tokens 32kk + 8g .. +7 of head 16 ht + n, 16 bytes.
+      // Four column groups' A operands are converted once and used against
+      // every head tile.
       {
         const int li = lane & 15;
-        const int bb = li >> 1;
-        const int e = li & 1;
-        const int tok = bb < 4 ? 4 * g + bb : 16 + 4 * (g ^ 2) + (bb - 4);
-        const uint8_t* vbase = pb.codes + tok * 16 + 8 * e;
-        auto rd = [&](int u) -> i32x2_t {   // unit u = 32 kk + c
-          const int kk = u / kDTiles, c = u % kDTiles;
-          return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (__attribute__((address_space(3))) i32x2_t*)(vbase + kk * (32 * 16) +
-                                                           c * (kS * 16)));
+        const uint8_t* vbase = pb.codes + (8 * g + (li >> 1)) * 16 + 8 * (li & 1) + cg0 * (kS * 16);
+        const uint8_t* pbase = pbuf + n * kPRow + 16 * g;
+        auto rdp = [&](int kk, int ht) -> f16x8_t {
+          return *reinterpret_cast<const f16x8_t*>(pbase + 16 * ht * kPRow + 64 * kk);
         };
-        constexpr int kPV = 2 * kDTiles;
-        i32x2_t rr[2] = {rd(0), rd(1)};
-        sfor<0, kPV>::run([&](auto I) {
-          constexpr int i = decltype(I)::value;
-          constexpr int kk = i / kDTiles;
-          constexpr int c = i % kDTiles;
-          const i32x2_t cw = rr[i & 1];
-          const f16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)cw.x, 1.0f, false);
-          const f16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)cw.x, 1.0f, true);
-          const f16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)cw.y, 1.0f, false);
-          const f16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)cw.y, 1.0f, true);
-          if constexpr (i + 2 < kPV) rr[i & 1] = rd(i + 2);
-          const f16x8_t av = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y, v3.x, v3.y};
-          // inline asm pins the accumulators to AGPRs, leaving the VGPRs to
-          // the score tiles; s_nop 1 covers a VALU write of av, pk or acc
-          // just before (two wait states)
-          if constexpr (HT == 2)
-            asm volatile("s_nop 1\n\t"
-                         "v_mfma_f32_16x16x32_f16 %0, %2, %3, %0\n\t"
-                         "v_mfma_f32_16x16x32_f16 %1, %2, %4, %1"
-                         : "+a"(acc[c][0]), "+a"(acc[c][1])
-                         : "v"(av), "v"(pk[kk][0]), "v"(pk[kk][1]));
-          else
-            asm volatile("s_nop 1\n\t"
-                         "v_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
-                         : "+a"(acc[c][0])
-                         : "v"(av), "v"(pk[kk][0]));
+        static_assert(CG == 4, "four column groups per wave");
+        sfor<0, 2>::run([&](auto KK) {
+          constexpr int kk = decltype(KK)::value;
+          f16x8_t pw[2];
+          pw[0] = rdp(kk, 0);
+          f16x8_t av[CG];
+#pragma unroll
+          for (int c = 0; c < CG; ++c) {
+            const i32x2_t cw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) i32x2_t*)(vbase + kk * (32 * 16) +
+                                                             c * (kS * 16)));
+            const f16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)cw.x, 1.0f, false);
+            const f16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)cw.x, 1.0f, true);
+            const f16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)cw.y, 1.0f, false);
+            const f16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)cw.y, 1.0f, true);
+            av[c] = f16x8_t{v0.x, v0.y, v1.x, v1.y, v2.x, v2.y, v3.x, v3.y};
+          }
           __builtin_amdgcn_sched_barrier(0);
+          sfor<0, NH>::run([&](auto H) {
+            constexpr int ht = decltype(H)::value;
+            if constexpr (ht + 1 < NH) pw[(ht + 1) & 1] = rdp(kk, ht + 1);
+            const f16x8_t pv = pw[ht & 1];
+            // inline asm pins the accumulators to AGPRs, leaving the VGPRs
+            // to the score tiles; s_nop 1 covers a VALU write of an operand
+            // just before (two wait states)
+            asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
+                         : "+a"(acc[0][ht]) : "v"(av[0]), "v"(pv));
+            asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
+                         : "+a"(acc[1][ht]) : "v"(av[1]), "v"(pv));
+            asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
+                         : "+a"(acc[2][ht]) : "v"(av[2]), "v"(pv));
+            asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
+                         : "+a"(acc[3][ht]) : "v"(av[3]), "v"(pv));
+            __builtin_amdgcn_sched_barrier(0);
+          });
         });
       }
     }
@@ -548,31 +595,22 @@ void latent_partial_kernel(LatArgs a) {
     // states; the compiler does not see the matrix-core writes in the asm)
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     // ---- partial of this fragment -------------------------------------------
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      l[ht] += shfl_xor_f32(l[ht], 16);
-      l[ht] += shfl_xor_f32(l[ht], 32);
-    }
+    l += shfl_xor_f32(l, 16);
+    l += shfl_xor_f32(l, 32);
     const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
-    if (any_bad) {
-      if (g == 0) {
+    if (!any_bad) {
+      // acc[c][ht] register r: dim 16(cg0 + c) + 4g + r of head 16 ht + n
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) prow[ht][kDv] = __builtin_nanf("");
-      }
-    } else {
-      // acc[c][ht] register r: dim 16c + 4g + r of head 16 ht + n
+      for (int c = 0; c < CG; ++c)
 #pragma unroll
-      for (int c = 0; c < kDTiles; ++c)
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-          *reinterpret_cast<f32x4_t*>(prow[ht] + 16 * c + 4 * g) = acc[c][ht];
-      if (g == 0) {
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-          prow[ht][kDv] = m[ht];
-          prow[ht][kDv + 1] = l[ht];
-        }
-      }
+          for (int ht = 0; ht < NH; ++ht)
+            *reinterpret_cast<f32x4_t*>(prow + 16 * ht * kRow + 16 * (cg0 + c) + 4 * g) = acc[c][ht];
+    }
+    if (qk && g == 0) {
+      // the running max and weight sum of this wave's QK head head0 + n
+      float* mrow = a.part + ((int64_t)(w + s) * a.Hq + head0 + n) * kRow;
+      mrow[kDv] = any_bad ? __builtin_nanf("") : m;
+      mrow[kDv + 1] = l;
     }
     gp = pref[s] + j1;
     __syncthreads();
@@ -644,23 +682,20 @@ size_t lat_slot_bytes(const pda_attn_shape& sh) {
 }
 
 size_t lat_lds_bytes(int B) {
-  return 2 * sizeof(PageBuf) + (size_t)kMaxTilesL * kQLdsTile +
-         (size_t)(kMaxThreadsL + 1 + B + 1) * sizeof(int);
+  return 2 * sizeof(PageBuf) + (size_t)kMaxWavesL * kQLdsWave + (size_t)kMaxHeadsL * kPRow +
+         (size_t)kMaxHeadsL * sizeof(float) +
+         (size_t)(kMaxWavesL + kMaxThreadsL + 1 + B + 1) * sizeof(int);
 }
 
 typedef void (*lat_kernel_t)(LatArgs);
 
-// 16 heads per wave, two waves per SIMD at 128 heads (one wave of 32 heads
-// per SIMD, HT = 2, measured 4 % slower on 64 sequences x 128 heads)
-constexpr int kHT = 1;
-constexpr int kHeadsPerWave = 16 * kHT;
-
-lat_kernel_t pick_latent(int nw) {
-  switch (nw) {
-    case 2: return latent_partial_kernel<2, kHT>;
-    case 4: return latent_partial_kernel<4, kHT>;
-    case 6: return latent_partial_kernel<6, kHT>;
-    default: return latent_partial_kernel<8, kHT>;
+// head tiles of 16 query heads (Hq / 16)
+lat_kernel_t pick_latent(int nh) {
+  switch (nh) {
+    case 2: return latent_partial_kernel<2>;
+    case 4: return latent_partial_kernel<4>;
+    case 6: return latent_partial_kernel<6>;
+    default: return latent_partial_kernel<8>;
   }
 }
 
@@ -717,18 +752,25 @@ int latent_launch(const pda_attn_shape& sh, const void* q, const void* k_cache,
   a.P = sh.num_pages;
   a.max_blocks = sh.max_blocks_per_seq;
   a.sm_scale = sh.sm_scale;
-  const int nw = sh.num_q_heads / kHeadsPerWave;
+  const int nh = sh.num_q_heads / 16;
   const size_t lds = lat_lds_bytes(sh.num_seqs);
-  lat_kernel_t k = pick_latent(nw);
-  static std::once_flag once[kMaxWavesL];
-  bool attr_ok = true;
-  std::call_once(once[nw - 1], [&] {
-    attr_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)lat_lds_bytes(kMaxSeqsL)) == hipSuccess;
-  });
-  if (!attr_ok) return PDA_ERR_LAUNCH;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(64 * nw), lds, stream, a);
+  lat_kernel_t k = pick_latent(nh);
+  // the dynamic LDS limit, raised once per kernel and device
+  static std::mutex mu;
+  static bool raised[kMaxWavesL + 1][64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return PDA_ERR_LAUNCH;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (!raised[nh][dev]) {
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lat_lds_bytes(kMaxSeqsL)) != hipSuccess)
+        return PDA_ERR_LAUNCH;
+      raised[nh][dev] = true;
+    }
+  }
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(64 * kMaxWavesL), lds, stream, a);
   if (hipGetLastError() != hipSuccess) return PDA_ERR_LAUNCH;
   hipLaunchKernelGGL(latent_combine_kernel, dim3((unsigned)(sh.num_seqs * (sh.num_q_heads / 4))),
                      dim3(256), 0, stream, a);

@@ -1,6 +1,6 @@
 // probe.hip — read-only HBM bandwidth probe (a measurement aid, not part of
 // the decode path): streaming or scrambled-chunk reads of a buffer, 16 bytes
-// per lane per load, eight loads in flight per lane.
+// per lane per load, sixteen loads in flight per lane.
 #include "pda_internal.h"
 #include "pda_probe.h"
 
@@ -8,35 +8,40 @@ namespace pda {
 namespace {
 
 constexpr int kProbeThreads = 256;
-constexpr int kProbeBlocksPerCu = 8;
+constexpr int kProbeBlocksPerCu = 32;
+constexpr int kProbeU = 16;   // 16-byte loads per lane in flight: 16 KB per wave
 
+// Each wave reads whole 16 KB blocks of the logical order (lane l, load u:
+// 16-byte element 64 u + l of the block, so every load instruction of a wave
+// covers 1 KB contiguous), blocks dealt round-robin over all waves.
+// Logical element i is physical element i (streaming) or, in chunked mode,
+// element i of scrambled chunk (i / chunk * 0x9E3779B1) mod nchunks.
+// (Measured on MI355X against one element per lane with the grid as the
+// stride, the form this replaces: 6.3 against 5.5 TB/s streaming.)
 __global__ __launch_bounds__(kProbeThreads) void hbm_read_kernel(const uint4* __restrict__ buf,
                                                                  int64_t n16, int64_t chunk16,
                                                                  int64_t nchunks,
                                                                  uint32_t* __restrict__ sink) {
   uint32_t acc = 0;
-  const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
-  const int64_t t = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x;
-  constexpr int U = 8;
-  for (int64_t i0 = t; i0 < n16; i0 += stride * U) {
-    uint4 v[U];
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * (kProbeThreads / 64);
+  const int64_t w = (int64_t)blockIdx.x * (kProbeThreads / 64) + (threadIdx.x >> 6);
+  const int64_t nblk = n16 / (64 * kProbeU);   // the host checks n16 % (64 * kProbeU) == 0
+  for (int64_t b = w; b < nblk; b += nw) {
+    uint4 v[kProbeU];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t i = i0 + (int64_t)u * stride;
-      if (i < n16) {
-        int64_t j = i;
-        if (chunk16 > 0) {   // chunk c of the pass reads scrambled chunk (c * odd) mod nchunks
-          const int64_t c = i / chunk16;
-          const int64_t sc = (int64_t)(((uint64_t)c * 0x9E3779B1ull) & (uint64_t)(nchunks - 1));
-          j = sc * chunk16 + (i - c * chunk16);
-        }
-        v[u] = buf[j];
-      } else {
-        v[u] = make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < kProbeU; ++u) {
+      const int64_t i = b * (64 * kProbeU) + u * 64 + lane;
+      int64_t j = i;
+      if (chunk16 > 0) {
+        const int64_t c = i / chunk16;
+        const int64_t sc = (int64_t)(((uint64_t)c * 0x9E3779B1ull) & (uint64_t)(nchunks - 1));
+        j = sc * chunk16 + (i - c * chunk16);
       }
+      v[u] = buf[j];
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    for (int u = 0; u < kProbeU; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   // one word per workgroup
   acc = (uint32_t)__builtin_amdgcn_readfirstlane((int)acc);
@@ -67,9 +72,8 @@ extern "C" int pda_hbm_read_probe(const void* buf, size_t bytes, int32_t chunk_b
     nchunks = (int64_t)(bytes / (size_t)chunk_bytes);
     if ((nchunks & (nchunks - 1)) != 0) return PDA_ERR_INVALID_ARG;
     chunk16 = chunk_bytes / 16;
-  } else if (bytes % 16 != 0) {
-    return PDA_ERR_INVALID_ARG;
   }
+  if (bytes % (16 * 64 * kProbeU) != 0) return PDA_ERR_INVALID_ARG;
   const int grid = device_cu_count() * kProbeBlocksPerCu;
   hipLaunchKernelGGL(hbm_read_kernel, dim3(grid), dim3(kProbeThreads), 0, as_stream(stream),
                      static_cast<const uint4*>(buf), (int64_t)(bytes / 16), chunk16, nchunks,

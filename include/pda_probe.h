@@ -16,7 +16,8 @@ extern "C" {
 /*
  * pda_hbm_read_probe — read every byte of a device buffer once.
  *  buf          device buffer of `bytes` bytes, 16-byte aligned; bytes a
- *               multiple of chunk_bytes (or of 16 when chunk_bytes == 0).
+ *               multiple of 16 KiB (the block one wave reads per step) and
+ *               of chunk_bytes.
  *  chunk_bytes  0: one streaming pass in address order. Else a power of two
  *               in [256, 65536]: the buffer is read as chunks of that size
  *               in a scrambled order (chunk i -> (i * 0x9E3779B1) mod the
