@@ -135,6 +135,29 @@ struct PageBuf {
   float sraw[kS];  // the page's scales as stored (copied with the codes)
 };
 
+// Maximum (sum) of a value over the four 16-lane rows of a wave, in every
+// lane of the column: the row swaps of gfx950 (rows 2i+1 of one register
+// with rows 2i of another, then the upper 32 lanes of one with the lower 32
+// of the other) pair each lane with the same column of the other rows: two
+// VALU swaps instead of two LDS permute round trips. Inline asm: the
+// compiler folds the builtin swap of two equal values as if it changed
+// nothing, and pads nothing around inline asm, so the two wait states before
+// each swap (its sources were just written by VALU) are padded here.
+__device__ __forceinline__ float rows_max(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  float c = fmaxf(a, b), d = c;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(c), "+v"(d));
+  return fmaxf(c, d);
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  float c = a + b, d = c;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(c), "+v"(d));
+  return c + d;
+}
+
 // The PV product is split by value dims over the workgroup's eight waves:
 // wave w owns the four 16-dim column groups 4w .. 4w+3 (dims 64w .. +63).
 constexpr int kPvGroups = kDTiles / kMaxWavesL;
@@ -346,8 +369,7 @@ void latent_partial_kernel(LatArgs a) {
     // bytes land at the wave-uniform LDS address + 16 * lane), so staging
     // takes no registers. The copy of page j+1 runs while page j computes.
     constexpr int kWaveChunks = kPageBytes / (16 * 64);    // 36 wave copies
-    auto fetch = [&](int j, PageBuf& pb) {
-      int page = btrow[j];
+    auto fetch = [&](int page, PageBuf& pb) {
       if (page < 0 || page >= a.P) {
         bad = true;
         page = 0;
@@ -414,7 +436,13 @@ void latent_partial_kernel(LatArgs a) {
       }
     };
 
-    fetch(j0, buf[0]);
+    // physical page ids are read one page ahead of their copies, through
+    // scalar loads (a block-table read just before the copy stalled every
+    // page by a memory round trip)
+    typedef const int32_t __attribute__((address_space(4))) ci32l_t;
+    ci32l_t* btc = (ci32l_t*)(uintptr_t)btrow;
+    int pid_next = j0 + 1 < j1 ? btc[j0 + 1] : 0;
+    fetch(btc[j0], buf[0]);
     for (int j = j0; j < j1; ++j) {
       PageBuf& pb = buf[(j - j0) & 1];
       // page j's copy (and every earlier load) complete, then publish; past
@@ -428,7 +456,8 @@ void latent_partial_kernel(LatArgs a) {
       // the next page, except the rare rescale: a wait there would wait for
       // the whole copy and serialise it with this page's products.
       finish(j, pb);
-      if (j + 1 < j1) fetch(j + 1, buf[(j + 1 - j0) & 1]);
+      if (j + 1 < j1) fetch(pid_next, buf[(j + 1 - j0) & 1]);
+      pid_next = j + 2 < j1 ? btc[j + 2] : 0;
       __syncthreads();
 
       if (qk) {
@@ -496,8 +525,7 @@ void latent_partial_kernel(LatArgs a) {
           bm = fmaxf(bm, v);
         }
       }
-      bm = fmaxf(bm, shfl_xor_f32(bm, 16));
-      bm = fmaxf(bm, shfl_xor_f32(bm, 32));
+      bm = rows_max(bm);
       // the running max moves only when the page's max exceeds it by more
       // than the threshold; alpha rescales what was summed under the old max
       const bool mv = bm > m + kTauL;
@@ -595,8 +623,7 @@ void latent_partial_kernel(LatArgs a) {
     // states; the compiler does not see the matrix-core writes in the asm)
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     // ---- partial of this fragment -------------------------------------------
-    l += shfl_xor_f32(l, 16);
-    l += shfl_xor_f32(l, 32);
+    l = rows_sum(l);
     const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
     if (!any_bad) {
       // acc[c][ht] register r: dim 16(cg0 + c) + 4g + r of head 16 ht + n
