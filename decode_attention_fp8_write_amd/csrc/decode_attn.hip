@@ -792,75 +792,115 @@ __device__ void process_item(const AttnArgs& a, int s, int c, int g, int chunk, 
     // the item's first block (m = -inf, l = acc = 0) every row's maximum is
     // taken up front, all rows in one interleaved reduction, so no row
     // takes the one-row path there.
-    const bool tok_ok = (b0 + lane) < tok1;
-    if (b0 == tok0) {
-      float t[G], bm[G];
+    // The tail block (tokens at or past tok1 among its 64) takes a copy of
+    // the softmax that masks them; full blocks carry no masks.
+    // Per-row factor of the accumulators for this block (1 unless the
+    // running max moved). It is applied to every row of every block,
+    // outside the rare branch that computes it: multiplying there made the
+    // compiler keep the accumulators in two sets of registers and copy them
+    // on every block.
+    float alpha[G];
+    auto softmax = [&](auto TAILC) {
+      constexpr bool TAIL = decltype(TAILC)::value;
+      const bool tok_ok = !TAIL || (b0 + lane) < tok1;
+      if (b0 == tok0) {
+        float t[G], bm[G];
 #pragma unroll
-      for (int r = 0; r < G; ++r) t[r] = (tail && !tok_ok) ? -INFINITY : z[r] * kmul;
-      wave_reduce_rows<false, G>(t, bm);
+        for (int r = 0; r < G; ++r) t[r] = (TAIL && !tok_ok) ? -INFINITY : z[r] * kmul;
+        wave_reduce_rows<false, G>(t, bm);
 #pragma unroll
-      for (int r = 0; r < G; ++r) m[r] = bm[r];
-    }
-    float zl[G];
-    uint64_t over = 0;
+        for (int r = 0; r < G; ++r) m[r] = bm[r];
+      }
+      float zl[G];
+      uint64_t over = 0;
 #pragma unroll
-    for (int r = 0; r < G; ++r) {
-      zl[r] = fmaf(z[r], kmul, -m[r]);
-      if (tail && !tok_ok) zl[r] = -INFINITY;
-      over |= __ballot(zl[r] > kTau);
-    }
-    if (over != 0) {
+      for (int r = 0; r < G; ++r) alpha[r] = 1.0f;
 #pragma unroll
       for (int r = 0; r < G; ++r) {
-        if (__ballot(zl[r] > kTau) != 0) {
-          const float bm = wave_max((tail && !tok_ok) ? -INFINITY : z[r] * kmul);
-          const float alpha = __builtin_amdgcn_exp2f(m[r] - bm);
-          m[r] = bm;
-          l[r] *= alpha;
-          acc[r][0] *= alpha;
-          acc[r][1] *= alpha;
-          zl[r] = (tail && !tok_ok) ? -INFINITY : fmaf(z[r], kmul, -bm);
+        zl[r] = fmaf(z[r], kmul, -m[r]);
+        if (TAIL && !tok_ok) zl[r] = -INFINITY;
+        over |= __ballot(zl[r] > kTau);
+      }
+      if (over != 0) {
+#pragma unroll
+        for (int r = 0; r < G; ++r) {
+          if (__ballot(zl[r] > kTau) != 0) {
+            const float bm = wave_max((TAIL && !tok_ok) ? -INFINITY : z[r] * kmul);
+            alpha[r] = as_f32(__builtin_amdgcn_readfirstlane(
+                (int)as_u32(__builtin_amdgcn_exp2f(m[r] - bm))));
+            m[r] = bm;
+            l[r] *= alpha[r];
+            zl[r] = (TAIL && !tok_ok) ? -INFINITY : fmaf(z[r], kmul, -bm);
+          }
         }
       }
-    }
-    // p of this lane's token for every row, to the wave's LDS buffer: FP8
-    // as [t/8][r][t%8] (f16, the order pv_block_fp8 reads), BF16 as
-    // pw[r*64 + t] with hi/lo bf16 parts at pw and pw + G*64.
+      // p of this lane's token for every row, to the wave's LDS buffer: FP8
+      // as [t/8][r][t%8] (f16, the order pv_block_fp8 reads), BF16 as
+      // pw[r*64 + t] with hi/lo bf16 parts at pw and pw + G*64.
 #pragma unroll
-    for (int r = 0; r < G; ++r) {
-      const float p = __builtin_amdgcn_exp2f(zl[r]);
-      l[r] += p;
-      if constexpr (FP8) {
-        pw[(lane / 8) * (8 * G) + r * 8 + (lane % 8)] = __builtin_bit_cast(uint16_t, (_Float16)p);
-      } else {
-        const uint32_t pu = as_u32(p);
-        const float rem = p - as_f32(pu & 0xFFFF0000u);
-        pw[r * 64 + lane] = (uint16_t)(pu >> 16);
-        pw[G * 64 + r * 64 + lane] = (uint16_t)(as_u32(rem) >> 16);
+      for (int r = 0; r < G; ++r) {
+        const float p = __builtin_amdgcn_exp2f(zl[r]);
+        l[r] += p;
+        if constexpr (FP8) {
+          pw[(lane / 8) * (8 * G) + r * 8 + (lane % 8)] = __builtin_bit_cast(uint16_t, (_Float16)p);
+        } else {
+          const uint32_t pu = as_u32(p);
+          const float rem = p - as_f32(pu & 0xFFFF0000u);
+          pw[r * 64 + lane] = (uint16_t)(pu >> 16);
+          pw[G * 64 + r * 64 + lane] = (uint16_t)(as_u32(rem) >> 16);
+        }
       }
-    }
-    // The wave's own LDS writes above must land before its reads below.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    // The wave's own LDS writes of p must land before its reads in PV.
+    auto lds_fence = [] {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
 
     // ---- PV: lane = dims (2*lane, 2*lane+1), all 64 tokens ---------------
     // In the tail block, tokens at or beyond tok1 have p = 0 but their V
-    // codes may be stale or poisoned (NaN * 0 = NaN): they are zeroed after
-    // conversion, in a separate instantiation of the loop.
-    // (the empty asm keeps the two copies from being merged back into one)
-    if (tail) {
-      asm volatile("" ::: "memory");
-      if constexpr (FP8)
-        pv_block_fp8<G, true>(vv, pw, acc, tok1 - b0);
-      else
-        pv_block<G, FP8, true>(vv, pw, acc, tok1 - b0);
+    // codes may be stale or poisoned (NaN * 0 = NaN). FP8: their bytes of
+    // the V words are zeroed first (in place), so one copy of PV serves
+    // every block (a second, masking copy made the compiler keep the
+    // accumulators in two sets of registers and copy them twice per block).
+    // BF16: the values are zeroed inside a separate copy of the loop (the
+    // register budget of two waves per SIMD holds it there).
+    if constexpr (FP8) {
+      if (tail) {
+        softmax(std::true_type{});
+        const int valid = tok1 - b0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+          asm volatile("v_and_b32 %0, %0, %1" : "+v"(vv[i]) : "v"(code_pair_mask(i, valid)));
+      } else {
+        softmax(std::false_type{});
+      }
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        acc[r][0] *= alpha[r];
+        acc[r][1] *= alpha[r];
+      }
+      lds_fence();
+      pv_block_fp8<G, false>(vv, pw, acc, 64);
     } else {
-      asm volatile("" ::: "memory");
-      if constexpr (FP8)
-        pv_block_fp8<G, false>(vv, pw, acc, 64);
+      if (tail)
+        softmax(std::true_type{});
       else
+        softmax(std::false_type{});
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        acc[r][0] *= alpha[r];
+        acc[r][1] *= alpha[r];
+      }
+      lds_fence();
+      if (tail) {
+        asm volatile("" ::: "memory");
+        pv_block<G, FP8, true>(vv, pw, acc, tok1 - b0);
+      } else {
+        asm volatile("" ::: "memory");
         pv_block<G, FP8, false>(vv, pw, acc, 64);
+      }
     }
     if (!has_next) break;
     load_v<G, FP8, S>(a, g, npg, vv);
