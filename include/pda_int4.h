@@ -7,7 +7,8 @@
  * weights for decode next to the FP8 KV cache (aifeed.sk, "Cloudflare
  * zrýchľuje inferenciu modelov Kimi a GLM kompresiou cache a váh", section
  * "Kompresia sa oplatí inde pri vstupe a inde pri výstupe"; the German page
- * "Cloudflare-Optimierungen für Kimi und GLM", section "GLM-
+ * "Cloudflare: Kleinere Modellbereitstellung senkt Speicherbedarf, doch
+ * Sicherheit wird zum Prüfstein" (remio.ai), section "GLM-
  * Gewichtskomprimierung verschiebt den Phasen-Trade-off"). The pages fix no
  * format. The one taken here: signed two's-complement 4-bit codes with one
  * scale per 128 consecutive inputs of each output row.

@@ -117,7 +117,8 @@ void oracle_paged_decode_attn(
  * streamed from memory for every generated token (aifeed.sk, "Cloudflare
  * zrýchľuje inferenciu modelov Kimi a GLM kompresiou cache a váh", section
  * "Kompresia sa oplatí inde pri vstupe a inde pri výstupe"; the German page
- * "Cloudflare-Optimierungen für Kimi und GLM", section "GLM-
+ * "Cloudflare: Kleinere Modellbereitstellung senkt Speicherbedarf, doch
+ * Sicherheit wird zum Prüfstein" (remio.ai), section "GLM-
  * Gewichtskomprimierung verschiebt den Phasen-Trade-off"). They fix no
  * format; the reading taken here: weight W[n][kk] = q[n][kk] * scale[n][kk/G]
  * with q a signed two's-complement 4-bit code, eight codes per uint32 word
