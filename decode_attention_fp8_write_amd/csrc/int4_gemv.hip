@@ -16,12 +16,11 @@
 // matrix-core kernel (below) whose products are nearly free, so both are
 // limited by unpacking the codes and by moving bytes, not by arithmetic.
 //
-// Mapping. A workgroup of four waves owns 16 output rows, four per wave.
-// Lane l of a wave takes chunks l, l+64, ... of k, 32 elements each (one
-// 16-byte load per row) for up to two tokens, 16 elements (8 bytes) for more,
-// where the activations take the registers; so the wave reads 1 KB or 512 B
-// of each row per load instruction, and several chunks' loads are issued
-// before their use. A chunk lies inside one 128-element scale group.
+// Mapping (one token). A workgroup of four waves owns 16 output rows, four
+// per wave. Lane l of a wave takes chunks l, l+64, ... of k, 32 elements
+// each (one 16-byte load per row), so the wave reads 1 KB of each row per
+// load instruction, and four chunks' loads are issued before their use. A
+// chunk lies inside one 128-element scale group.
 //
 // Unpacking without integer-to-float conversions: a code u' = q + 8 in
 // [0, 15] (the two's-complement code with its top bit flipped) put into the
@@ -36,9 +35,6 @@
 // Nibble j of a word and nibble j + 4 land in the two halves of one dword
 // ((word >> 4j) & 0x000F000F), so activations are paired the same way:
 // (x_j, x_{j+4}) by one byte permute per pair.
-//
-// Tokens (vector-ALU kernel): up to kMaxTok tokens per grid row; grid.y
-// covers larger batches, each grid row streaming the weights again.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -55,7 +51,7 @@ constexpr int kGroup = 128;
 constexpr int kRowsPerWave = 4;
 constexpr int kWaves = 4;
 constexpr int kRowsPerBlock = kRowsPerWave * kWaves;
-constexpr int kMaxTok = 8;
+constexpr int kChunk = 32;                 // k elements per lane and chunk
 constexpr uint32_t kMagic = 0x43004300u;   // bf16 pair (128.0, 128.0)
 constexpr uint32_t kOnes = 0x3F803F80u;    // bf16 pair (1.0, 1.0)
 
@@ -78,24 +74,18 @@ __device__ __forceinline__ void pair_up(const uint4 X, uint32_t p[4]) {
   p[3] = __builtin_amdgcn_perm(X.w, X.y, 0x07060302u);
 }
 
-template <int MT>
 __global__ __launch_bounds__(64 * kWaves) void int4_gemv_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ w,
-    const uint16_t* __restrict__ scale, int m, int n, int k, float* __restrict__ y) {
+    const uint16_t* __restrict__ scale, int n, int k, float* __restrict__ y) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int row0 = blockIdx.x * kRowsPerBlock + wave * kRowsPerWave;
-  const int tok0 = blockIdx.y * kMaxTok;
-  // CW packed words (8*CW elements) per lane and chunk: 16-byte weight loads
-  // where few tokens leave registers to spare, 8-byte loads otherwise
-  constexpr int CW = MT <= 2 ? 4 : 2;
-  constexpr int CH = 8 * CW;
-  const int chunks = k / CH;
+  const int chunks = k / kChunk;
   const int words = k / 8;
   const int groups = k / kGroup;
 
-  // rows past n read row n-1 and are not stored; tokens past m read token
-  // m-1 and are not stored, so every load stays inside its buffer
+  // rows past n read row n-1 and are not stored, so every load stays inside
+  // its buffer
   const uint32_t* wr[kRowsPerWave];
   const uint16_t* sr[kRowsPerWave];
 #pragma unroll
@@ -104,102 +94,77 @@ __global__ __launch_bounds__(64 * kWaves) void int4_gemv_kernel(
     wr[r] = w + (int64_t)row * words;
     sr[r] = scale + (int64_t)row * groups;
   }
-  const uint16_t* xt[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) xt[t] = x + (int64_t)min(tok0 + t, m - 1) * k;
 
-  float acc[kRowsPerWave][MT];
+  float acc[kRowsPerWave];
 #pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[r][t] = 0.0f;
+  for (int r = 0; r < kRowsPerWave; ++r) acc[r] = 0.0f;
 
   // U chunks per lane per step, all their loads issued before any use, so
   // enough bytes are in flight to cover HBM latency with few waves per CU
-  constexpr int U = MT <= 2 ? 4 : (MT == 4 ? 2 : 1);
+  constexpr int U = 4;
   for (int c0 = lane; c0 < chunks; c0 += 64 * U) {
-    uint32_t wq[U][kRowsPerWave][CW];
+    uint4 wq[U][kRowsPerWave];
     float sc[U][kRowsPerWave];
-    uint4 xv[U][MT][CW];
+    uint4 xv[U][4];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + 64 * u;
       if (c < chunks) {
 #pragma unroll
         for (int r = 0; r < kRowsPerWave; ++r) {
-          if constexpr (CW == 4) {
-            const uint4 v = *reinterpret_cast<const uint4*>(wr[r] + CW * c);
-            wq[u][r][0] = v.x; wq[u][r][1] = v.y; wq[u][r][2] = v.z; wq[u][r][3] = v.w;
-          } else {
-            const uint2 v = *reinterpret_cast<const uint2*>(wr[r] + CW * c);
-            wq[u][r][0] = v.x; wq[u][r][1] = v.y;
-          }
-          sc[u][r] = bf16_bits_to_f32(sr[r][c / (kGroup / CH)]);
+          wq[u][r] = *reinterpret_cast<const uint4*>(wr[r] + 4 * c);
+          sc[u][r] = bf16_bits_to_f32(sr[r][c / (kGroup / kChunk)]);
         }
+        const uint4* xs = reinterpret_cast<const uint4*>(x + kChunk * c);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          const uint4* xs = reinterpret_cast<const uint4*>(xt[t] + CH * c);
-#pragma unroll
-          for (int i = 0; i < CW; ++i) xv[u][t][i] = xs[i];
-        }
+        for (int i = 0; i < 4; ++i) xv[u][i] = xs[i];
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (c0 + 64 * u >= chunks) break;
-      // activation pairs and -136 * sum x of the chunk, per token
-      uint32_t xp[MT][4 * CW];
-      float base[MT];
+      // activation pairs and -136 * sum x of the chunk
+      uint32_t xp[16];
+      float s = 0.0f;
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        float s = 0.0f;
-#pragma unroll
-        for (int i = 0; i < CW; ++i) {
-          const uint4 a = xv[u][t][i];
-          pair_up(a, xp[t] + 4 * i);
-          s = dot2(a.x, kOnes, s);
-          s = dot2(a.y, kOnes, s);
-          s = dot2(a.z, kOnes, s);
-          s = dot2(a.w, kOnes, s);
-        }
-        base[t] = -136.0f * s;
+      for (int i = 0; i < 4; ++i) {
+        const uint4 a = xv[u][i];
+        pair_up(a, xp + 4 * i);
+        s = dot2(a.x, kOnes, s);
+        s = dot2(a.y, kOnes, s);
+        s = dot2(a.z, kOnes, s);
+        s = dot2(a.w, kOnes, s);
       }
+      const float base = -136.0f * s;
 #pragma unroll
       for (int r = 0; r < kRowsPerWave; ++r) {
-        uint32_t wb[4 * CW];
+        const uint32_t q[4] = {wq[u][r].x, wq[u][r].y, wq[u][r].z, wq[u][r].w};
+        uint32_t wb[16];
 #pragma unroll
-        for (int i = 0; i < CW; ++i) {
-          const uint32_t v = wq[u][r][i] ^ 0x88888888u;
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t v = q[i] ^ 0x88888888u;
 #pragma unroll
           for (int j = 0; j < 4; ++j) wb[4 * i + j] = ((v >> (4 * j)) & 0x000F000Fu) | kMagic;
         }
+        float d = base;
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          float d = base[t];
-#pragma unroll
-          for (int i = 0; i < 4 * CW; ++i) d = dot2(wb[i], xp[t][i], d);
-          acc[r][t] = __builtin_fmaf(d, sc[u][r], acc[r][t]);
-        }
+        for (int i = 0; i < 16; ++i) d = dot2(wb[i], xp[i], d);
+        acc[r] = __builtin_fmaf(d, sc[u][r], acc[r]);
       }
     }
   }
 
   // sum over the 64 lanes; afterwards every lane holds every total
 #pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r)
+  for (int r = 0; r < kRowsPerWave; ++r) {
+    float v = acc[r];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      float v = acc[r][t];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-      acc[r][t] = v;
-    }
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    acc[r] = v;
+  }
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r)
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-      if (lane == r * MT + t && row0 + r < n && tok0 + t < m)
-        y[(int64_t)(tok0 + t) * n + row0 + r] = acc[r][t];
+    if (lane == r && row0 + r < n) y[row0 + r] = acc[r];
 }
 
 // ---- matrix-core path for two or more tokens ---------------------------
@@ -225,8 +190,6 @@ constexpr int kRT = 2;              // 16-row tiles per workgroup
 constexpr int kMfmaRows = 16 * kRT;
 constexpr int kMfmaTok = 32;        // tokens per grid row (two 16-token tiles)
 constexpr uint32_t k136 = 0x43084308u;   // bf16 pair (136.0, 136.0)
-// batches from this many tokens take the matrix-core kernel
-constexpr int kMfmaMinTokens = 2;
 
 template <int TILES, int NW>
 __global__ __launch_bounds__(64 * NW) void int4_gemm_mfma_kernel(
@@ -372,35 +335,24 @@ extern "C" int int4_gemv_bf16(const void* x, const uint32_t* w, const void* scal
   if ((reinterpret_cast<uintptr_t>(x) & 15) != 0 || (reinterpret_cast<uintptr_t>(w) & 15) != 0 ||
       (reinterpret_cast<uintptr_t>(scale) & 1) != 0 || (reinterpret_cast<uintptr_t>(y) & 3) != 0)
     return PDA_ERR_INVALID_ARG;
+  // one token: grid of 16-row workgroups; more: 32-row by 32-token tiles
   const int64_t blocks = ((int64_t)n + kRowsPerBlock - 1) / kRowsPerBlock;
-  const int64_t tok_blocks = ((int64_t)m + kMaxTok - 1) / kMaxTok;
-  if (blocks > 0x7FFFFFFF || tok_blocks > 65535) return PDA_ERR_UNSUPPORTED;
+  const int64_t tok_tiles = ((int64_t)m + kMfmaTok - 1) / kMfmaTok;
+  if (blocks > 0x7FFFFFFF || tok_tiles > 65535) return PDA_ERR_UNSUPPORTED;
   hipStream_t s = as_stream(stream);
-  const auto* xb0 = static_cast<const uint16_t*>(x);
-  const auto* sb0 = static_cast<const uint16_t*>(scale);
-  if (m >= kMfmaMinTokens) {
-    const dim3 g2((unsigned)(((int64_t)n + kMfmaRows - 1) / kMfmaRows),
-                  (unsigned)(((int64_t)m + kMfmaTok - 1) / kMfmaTok));
-    if (m <= 16)
-      hipLaunchKernelGGL((int4_gemm_mfma_kernel<1, 8>), g2, dim3(64 * 8), 0, s, xb0, w, sb0, m,
-                         n, k, y);
-    else
-      hipLaunchKernelGGL((int4_gemm_mfma_kernel<2, 4>), g2, dim3(64 * 4), 0, s, xb0, w, sb0, m,
-                         n, k, y);
-    return launch_status();
-  }
-  const dim3 grid((unsigned)blocks, (unsigned)tok_blocks);
-  const dim3 block(64 * kWaves);
-  const int mt = m < kMaxTok ? m : kMaxTok;
   const auto* xb = static_cast<const uint16_t*>(x);
   const auto* sb = static_cast<const uint16_t*>(scale);
-  if (mt == 1)
-    hipLaunchKernelGGL(int4_gemv_kernel<1>, grid, block, 0, s, xb, w, sb, m, n, k, y);
-  else if (mt == 2)
-    hipLaunchKernelGGL(int4_gemv_kernel<2>, grid, block, 0, s, xb, w, sb, m, n, k, y);
-  else if (mt <= 4)
-    hipLaunchKernelGGL(int4_gemv_kernel<4>, grid, block, 0, s, xb, w, sb, m, n, k, y);
-  else
-    hipLaunchKernelGGL(int4_gemv_kernel<8>, grid, block, 0, s, xb, w, sb, m, n, k, y);
+  if (m >= 2) {
+    const dim3 g2((unsigned)(((int64_t)n + kMfmaRows - 1) / kMfmaRows), (unsigned)tok_tiles);
+    if (m <= 16)
+      hipLaunchKernelGGL((int4_gemm_mfma_kernel<1, 8>), g2, dim3(64 * 8), 0, s, xb, w, sb, m, n,
+                         k, y);
+    else
+      hipLaunchKernelGGL((int4_gemm_mfma_kernel<2, 4>), g2, dim3(64 * 4), 0, s, xb, w, sb, m, n,
+                         k, y);
+    return launch_status();
+  }
+  hipLaunchKernelGGL(int4_gemv_kernel, dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, xb, w,
+                     sb, n, k, y);
   return launch_status();
 }

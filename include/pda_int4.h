@@ -40,7 +40,8 @@ extern "C" {
  * Asynchronous on `stream`; nothing is allocated. Returns 0,
  * PDA_ERR_INVALID_ARG (1) for negative sizes, NULL or misaligned pointers,
  * PDA_ERR_UNSUPPORTED (2) for group != 128, k not a positive multiple of 128
- * (k == 0 with m, n > 0 included) or more than 524280 tokens, PDA_ERR_LAUNCH
+ * (k == 0 with m, n > 0 included) or more than 2097120 tokens (65535
+ * grid rows of 32 tokens), PDA_ERR_LAUNCH
  * (3) on a launch failure. m == 0 or n == 0 does nothing.
  */
 int int4_gemv_bf16(const void* x, const uint32_t* w, const void* scale, int32_t m, int32_t n,

@@ -199,7 +199,7 @@ def test_int4_gemv_argument_checks(pda):
     assert g(f, ctypes.c_void_p(4104), f, 1, 16, 128, 128, f, null) == E
     assert g(f, f, ctypes.c_void_p(4097), 1, 16, 128, 128, f, null) == E   # scale odd
     assert g(f, f, f, 1, 16, 128, 128, ctypes.c_void_p(4098), null) == E   # y not 4-aligned
-    assert g(f, f, f, 524281, 16, 128, 128, f, null) == U    # too many tokens for the grid
+    assert g(f, f, f, 2097121, 16, 128, 128, f, null) == U   # too many tokens for the grid
 
 
 def test_noalloc_host_checks(pda):
