@@ -39,29 +39,34 @@ __global__ __launch_bounds__(kThreads) void validate_kernel(
   const int s = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int32_t* bt = block_table + (int64_t)s * max_blocks;
+  const uint32_t* ex = expected + (int64_t)s * max_blocks;
+  constexpr int kStride = kThreads;           // blocks between a wave's windows
+  // The first two windows' table entries and expected tags are read before
+  // the length is known (every index below max_blocks lies inside the
+  // sequence's row), so that the length and them arrive in one round trip;
+  // the length then masks them.
+  int w0 = wave * 64;
+  int32_t p0 = 0, p1 = 0;
+  uint32_t e0 = 0, e1 = 0;
+  if (w0 + lane < max_blocks) { p0 = bt[w0 + lane]; e0 = ex[w0 + lane]; }
+  if (w0 + kStride + lane < max_blocks) { p1 = bt[w0 + kStride + lane]; e1 = ex[w0 + kStride + lane]; }
   const int64_t len = lens[s];
   if (len < 0 || len > (int64_t)max_blocks * S) {
     if (threadIdx.x == 0) verdict[s] = -1;
     return;
   }
   const int n = (int)((len + S - 1) / S);
-  const int32_t* bt = block_table + (int64_t)s * max_blocks;
-  const uint32_t* ex = expected + (int64_t)s * max_blocks;
-  constexpr int kStride = kThreads;           // blocks between a wave's windows
   int first = INT_MAX;
-  for (int w0 = wave * 64; w0 < n; w0 += 2 * kStride) {
+  while (w0 < n) {
     const int j0 = w0 + lane, j1 = w0 + kStride + lane;
-    int32_t p0 = 0, p1 = 0;
-    uint32_t e0 = 0, e1 = 0;
-    if (j0 < n) { p0 = bt[j0]; e0 = ex[j0]; }
-    if (j1 < n) { p1 = bt[j1]; e1 = ex[j1]; }
     const bool r0 = j0 < n && (p0 < 0 || p0 >= P);
     const bool r1 = j1 < n && (p1 < 0 || p1 >= P);
     uint32_t t0 = e0, t1 = e1;
     if (j0 < n && !r0) t0 = page_tags[p0];
     if (j1 < n && !r1) t1 = page_tags[p1];
-    const uint64_t m0 = __ballot(r0 || t0 != e0);
-    const uint64_t m1 = __ballot(r1 || t1 != e1);
+    const uint64_t m0 = __ballot(j0 < n && (r0 || t0 != e0));
+    const uint64_t m1 = __ballot(j1 < n && (r1 || t1 != e1));
     if (m0 != 0) {
       first = w0 + __builtin_ctzll(m0);
       break;
@@ -70,6 +75,10 @@ __global__ __launch_bounds__(kThreads) void validate_kernel(
       first = w0 + kStride + __builtin_ctzll(m1);
       break;
     }
+    // the next two windows of this wave (sequences past 2 kThreads blocks)
+    w0 += 2 * kStride;
+    if (w0 + lane < n) { p0 = bt[w0 + lane]; e0 = ex[w0 + lane]; }
+    if (w0 + kStride + lane < n) { p1 = bt[w0 + kStride + lane]; e1 = ex[w0 + kStride + lane]; }
   }
   if (lane == 0) best[wave] = first;
   __syncthreads();
