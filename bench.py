@@ -20,7 +20,7 @@ on a bounded sample of the same workload on the host cores.
 Every timed figure is the median over N interleaved passes of exactly K
 calls between two HIP events on the launch stream (FP8 and BF16 steps, the
 attention calls alone, and the no-op-tracker step alternate within each
-round), after W warm-up steps. Extra keys: the latent workload's attention
+pass), after W warm-up steps. Extra keys: the latent workload's attention
 call against the matrix-core peak, the full-pool workload's step with the
 tag check's share, the BF16 -> FP8 page transcode, the INT4 GEMV.
 """

@@ -18,39 +18,37 @@
 // (workgroup + sequence), which is unique. The combine kernel merges the
 // fragments of each sequence with a log-sum-exp rule.
 //
-// Inside a fragment, one page (64 tokens) at a time:
-//  * the workgroup copies the page's 36 KB of codes into LDS by direct
-//    global->LDS copies, and its 64 scales (double-buffered: the next page's
-//    copy is issued as soon as the page's barrier is passed and runs while
-//    the current one is computed). Tokens past the end are written as zero codes
+// Inside a fragment, one page (64 tokens) at a time, by eight waves (two per
+// SIMD, so one wave's conversions and softmax overlap the other's matrix
+// products; a wave's own instruction stream is in order):
+//  * the workgroup copies the page's 36 KB of codes and its 64 scales into
+//    LDS by direct global->LDS copies (double-buffered: the next page's copy
+//    is issued once the page's first barrier is passed and runs while the
+//    current one is computed). Tokens past the end are written as zero codes
 //    with weight 0, so they contribute nothing and poisoned bytes are never
 //    read into the arithmetic.
-//  * wave w owns query heads [16w, 16w+16), one 16-head tile, so 128 heads
-//    take eight waves, two per SIMD: one wave's conversions and softmax
-//    overlap the other's matrix products (a wave's own instruction stream
-//    is in order). Every
-//    product runs on 16x16x32 matrix-core tiles, whose operand reads from
+//  * QK is split by heads: wave w < NH owns query heads [16w, 16w+16). S^T =
+//    K Q^T on v_mfma_f32_16x16x32_bf16: K codes convert exactly to bf16 (A
+//    operand, lane = token row, token tile t = tokens 16t .. 16t+15), Q is
+//    bf16 (B operand, lane = head; its first k-steps in registers, the rest
+//    in the wave's LDS region), so Q enters exactly. The operand reads from
 //    the token-major page hit every LDS bank once per half-wave (a lane reads
 //    8 bytes; the 32 lanes of a half-wave cover 16 tokens' full 16-byte
-//    slots, whose tokens differ mod 16).
-//  * QK as S^T = K Q^T on v_mfma_f32_16x16x32_bf16: K codes convert exactly
-//    to bf16 (A operand, lane = token row), Q stays resident in registers as
-//    bf16 (B operand, lane = head), so Q enters exactly. Token tile t holds
-//    tokens 16t .. 16t+15; in odd tiles row m is token 16t + (m ^ 8), so
-//    that each half-wave of the PV transpose read below also meets 16
-//    distinct token residues.
+//    slots).
 //  * softmax in log2 units with the per-token scale folded in: for token t
 //    with scale c_t, y = (q.code_t) * c_t * sm_scale * log2(e) + log2(c_t);
 //    p' = 2^(y - m) = c_t * e^(score - m'), so the weights already carry the
 //    value scale, and the running sum adds p' / c_t. The running max m only
-//    moves when a page's max exceeds it by more than 8 (p' <= 2^8).
-//  * PV as O^T = V^T P^T on v_mfma_f32_16x16x32_f16: V codes convert exactly
-//    to f16. The A operand needs eight tokens of one dim per lane; the LDS
-//    transpose read ds_read_b64_tr_b8 gathers them from the token-major page
-//    (in each 16-lane group, lane i receives byte i%8 of the eight 8-byte
-//    chunks addressed by lanes 2b + i/8). P^T is the B operand straight from
-//    the QK accumulator registers (k-step kk takes token tiles 2kk, 2kk+1):
-//    their token order fixes the order in which the transpose read gathers V.
+//    moves when a page's max exceeds it by more than 8 (p' <= 2^8). The
+//    weights go to LDS as f16, one 144-byte row per head.
+//  * PV is split by value dims: wave w owns dims [64w, 64w + 64) of every
+//    head, O^T = V^T P^T on v_mfma_f32_16x16x32_f16. The A operand needs
+//    eight tokens of one dim per lane; the LDS transpose read
+//    ds_read_b64_tr_b8 gathers them from the token-major page (in each
+//    16-lane group, lane i receives byte i%8 of the eight 8-byte chunks
+//    addressed by lanes 2b + i/8), and its codes convert exactly to f16 once
+//    per workgroup. The B operand is the weights of a head tile from LDS.
+//    The accumulators (64 dims x every head) stay in AGPRs.
 #include <mutex>
 #include <type_traits>
 
