@@ -16,11 +16,16 @@
 // matrix-core kernel (below) whose products are nearly free, so both are
 // limited by unpacking the codes and by moving bytes, not by arithmetic.
 //
-// Mapping (one token). A workgroup of four waves owns 16 output rows, four
-// per wave. Lane l of a wave takes chunks l, l+64, ... of k, 32 elements
-// each (one 16-byte load per row), so the wave reads 1 KB of each row per
-// load instruction, and four chunks' loads are issued before their use. A
-// chunk lies inside one 128-element scale group.
+// Mapping (one token). A workgroup of four waves owns 8 output rows, two per
+// wave. Lane l of a wave takes chunks l, l+64, ... of k, 32 elements each
+// (one 16-byte load per row), so the wave reads 1 KB of each row per load
+// instruction, and two chunks' loads are issued before their use. A chunk
+// lies inside one 128-element scale group. (Two rows and two chunks ahead
+// keep a wave at 89 VGPRs, so 8192 rows make four waves per SIMD: measured
+// 11.1-11.4 us against 13.4 us for four rows and four chunks ahead at 213
+// VGPRs, two waves per SIMD, on 8192 x 8192 weights. Pairing and summing the
+// activations once per workgroup in LDS instead of per wave was slower,
+// 11.8 us: the staging barrier costs more than the vector work it saves.)
 //
 // Unpacking without integer-to-float conversions: a code u' = q + 8 in
 // [0, 15] (the two's-complement code with its top bit flipped) put into the
@@ -48,7 +53,7 @@ namespace {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kGroup = 128;
-constexpr int kRowsPerWave = 4;
+constexpr int kRowsPerWave = 2;
 constexpr int kWaves = 4;
 constexpr int kRowsPerBlock = kRowsPerWave * kWaves;
 constexpr int kChunk = 32;                 // k elements per lane and chunk
@@ -99,9 +104,8 @@ __global__ __launch_bounds__(64 * kWaves) void int4_gemv_kernel(
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) acc[r] = 0.0f;
 
-  // U chunks per lane per step, all their loads issued before any use, so
-  // enough bytes are in flight to cover HBM latency with few waves per CU
-  constexpr int U = 4;
+  // U chunks per lane per step, all their loads issued before any use
+  constexpr int U = 2;
   for (int c0 = lane; c0 < chunks; c0 += 64 * U) {
     uint4 wq[U][kRowsPerWave];
     float sc[U][kRowsPerWave];
