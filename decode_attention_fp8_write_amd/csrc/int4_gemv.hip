@@ -39,7 +39,11 @@
 //
 // Nibble j of a word and nibble j + 4 land in the two halves of one dword
 // ((word >> 4j) & 0x000F000F), so activations are paired the same way:
-// (x_j, x_{j+4}) by one byte permute per pair.
+// (x_j, x_{j+4}) by one byte permute per pair. Flipping the code's top bit
+// and setting the exponent bits of 128.0 is one bitwise step on the masked
+// field, (field & 0x000F000F) ^ 0x43084308 (a single v_bitop3), so a word's
+// four dwords cost a shift and a bitop3 each (10.5-10.8 us against 11.0-11.6
+// us with a separate xor and or, 8192 x 8192).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -57,7 +61,12 @@ constexpr int kRowsPerWave = 2;
 constexpr int kWaves = 4;
 constexpr int kRowsPerBlock = kRowsPerWave * kWaves;
 constexpr int kChunk = 32;                 // k elements per lane and chunk
-constexpr uint32_t kMagic = 0x43004300u;   // bf16 pair (128.0, 128.0)
+// bf16 pair (128.0, 128.0) with bit 3 of each half set: (field & 0x000F000F)
+// ^ kMagicFlip flips the codes' top bits and sets the exponent bits of
+// 128.0 in one bitwise step (the mask keeps the code bits, the constant
+// supplies the rest)
+constexpr uint32_t kMagicFlip = 0x43084308u;
+constexpr uint32_t kNibbles = 0x000F000Fu;
 constexpr uint32_t kOnes = 0x3F803F80u;    // bf16 pair (1.0, 1.0)
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -146,9 +155,8 @@ __global__ __launch_bounds__(64 * kWaves) void int4_gemv_kernel(
         uint32_t wb[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t v = q[i] ^ 0x88888888u;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) wb[4 * i + j] = ((v >> (4 * j)) & 0x000F000Fu) | kMagic;
+          for (int j = 0; j < 4; ++j) wb[4 * i + j] = ((q[i] >> (4 * j)) & kNibbles) ^ kMagicFlip;
         }
         float d = base;
 #pragma unroll
@@ -178,24 +186,26 @@ __global__ __launch_bounds__(64 * kWaves) void int4_gemv_kernel(
 // element 2j+1 is k j+4 of the lane's 8), which the sum does not see. Lane
 // (c, g) of a wave holds, for k-step s of scale group G, words 4g + s of
 // the group in row c (its 16 bytes of the group are one load) and the
-// activations of the same 8 k. A second product against a constant 136
-// operand gives 136 * sum x of the same k, subtracted at the group's end
-// before the group scale: fresh accumulators per group, one fma per output.
-// A workgroup owns 32 rows (two 16-row tiles) and up to 32 tokens (grid
-// rows of 32 tokens run side by side and share the weights through the
-// caches); its NW waves take every NW-th scale group and meet in LDS at the
-// end: eight waves for one 16-token tile, four for two, whose registers
-// leave room for fewer waves (measured: eight waves 3-4 us faster up to 16
-// tokens, even at 32, slower at 64).
+// activations of the same 8 k. Products against a constant -136 operand
+// give -136 * sum x of each token over the group, which seeds the group's
+// accumulators, so they come out as x.q and take the group scale in one fma
+// per output (0.2-0.8 us faster on 8192 x 8192 than subtracting a separate
+// 136 * sum x product at the group's end).
+// A workgroup owns kRT 16-row tiles and up to 32 tokens (grid rows of 32
+// tokens run side by side and share the weights through the caches); its NW
+// waves take every NW-th scale group and meet in LDS at the end: eight waves
+// for one 16-token tile, four for two, whose registers leave room for fewer
+// waves (measured: eight waves 3-4 us faster up to 16 tokens, even at 32,
+// slower at 64). Every row block re-reads the activations, from L2: two row
+// tiles serve up to 32 tokens, four beyond (8192 x 8192, 64 tokens: 36.5 us
+// against 47.4 us with two; 32 tokens: 36.2 against 26.8; eight tiles 55 us).
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kRT = 2;              // 16-row tiles per workgroup
-constexpr int kMfmaRows = 16 * kRT;
 constexpr int kMfmaTok = 32;        // tokens per grid row (two 16-token tiles)
-constexpr uint32_t k136 = 0x43084308u;   // bf16 pair (136.0, 136.0)
+constexpr uint32_t kNeg136 = 0xC308C308u;   // bf16 pair (-136.0, -136.0)
 
-template <int TILES, int NW>
+template <int TILES, int NW, int kRT>
 __global__ __launch_bounds__(64 * NW) void int4_gemm_mfma_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ w,
     const uint16_t* __restrict__ scale, int m, int n, int k, float* __restrict__ y) {
@@ -203,7 +213,7 @@ __global__ __launch_bounds__(64 * NW) void int4_gemm_mfma_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const int row0 = blockIdx.x * kMfmaRows;
+  const int row0 = blockIdx.x * 16 * kRT;
   const int tok0 = blockIdx.y * kMfmaTok;
   const int groups = k / kGroup;
 
@@ -221,8 +231,8 @@ __global__ __launch_bounds__(64 * NW) void int4_gemm_mfma_kernel(
   for (int t = 0; t < TILES; ++t)
     xr[t] = x + (int64_t)min(tok0 + 16 * t + c, m - 1) * k + 32 * g;
 
-  const uint4 c136 = make_uint4(k136, k136, k136, k136);
-  const bf16x8_t b136 = __builtin_bit_cast(bf16x8_t, c136);
+  const uint4 cn136 = make_uint4(kNeg136, kNeg136, kNeg136, kNeg136);
+  const bf16x8_t bneg136 = __builtin_bit_cast(bf16x8_t, cn136);
   f32x4_t yacc[TILES][kRT];
 #pragma unroll
   for (int t = 0; t < TILES; ++t)
@@ -254,13 +264,24 @@ __global__ __launch_bounds__(64 * NW) void int4_gemm_mfma_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (g0 + NW * u >= groups) break;
-      f32x4_t am[TILES][kRT], ac[TILES];
+      // activation pairs of the group's four steps, then -136 * sum x of
+      // each token over the group, which seeds the group's products
+      bf16x8_t av[TILES][4];
+      f32x4_t nac[TILES];
 #pragma unroll
       for (int t = 0; t < TILES; ++t) {
-        ac[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) am[t][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < 4; ++s) {
+          uint32_t p[4];
+          pair_up(xv[u][t][s], p);
+          av[t][s] = __builtin_bit_cast(bf16x8_t, make_uint4(p[0], p[1], p[2], p[3]));
+        }
+        nac[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          nac[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[t][s], bneg136, nac[t], 0, 0, 0);
       }
+      f32x4_t am[TILES][kRT];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         bf16x8_t bw[kRT];
@@ -268,22 +289,17 @@ __global__ __launch_bounds__(64 * NW) void int4_gemm_mfma_kernel(
         for (int rt = 0; rt < kRT; ++rt) {
           const uint4 q = wv[u][rt];
           const uint32_t word = s == 0 ? q.x : s == 1 ? q.y : s == 2 ? q.z : q.w;
-          const uint32_t v = word ^ 0x88888888u;
-          const uint4 d = make_uint4((v & 0x000F000Fu) | kMagic, ((v >> 4) & 0x000F000Fu) | kMagic,
-                                     ((v >> 8) & 0x000F000Fu) | kMagic,
-                                     ((v >> 12) & 0x000F000Fu) | kMagic);
+          const uint4 d = make_uint4(
+              (word & kNibbles) ^ kMagicFlip, ((word >> 4) & kNibbles) ^ kMagicFlip,
+              ((word >> 8) & kNibbles) ^ kMagicFlip, ((word >> 12) & kNibbles) ^ kMagicFlip);
           bw[rt] = __builtin_bit_cast(bf16x8_t, d);
         }
 #pragma unroll
-        for (int t = 0; t < TILES; ++t) {
-          uint32_t p[4];
-          pair_up(xv[u][t][s], p);
-          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(p[0], p[1], p[2], p[3]));
+        for (int t = 0; t < TILES; ++t)
 #pragma unroll
           for (int rt = 0; rt < kRT; ++rt)
-            am[t][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw[rt], am[t][rt], 0, 0, 0);
-          ac[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b136, ac[t], 0, 0, 0);
-        }
+            am[t][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[t][s], bw[rt],
+                                                                s == 0 ? nac[t] : am[t][rt], 0, 0, 0);
       }
 #pragma unroll
       for (int t = 0; t < TILES; ++t)
@@ -292,7 +308,7 @@ __global__ __launch_bounds__(64 * NW) void int4_gemm_mfma_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             yacc[t][rt][r] =
-                __builtin_fmaf(am[t][rt][r] - ac[t][r], sc[u][rt], yacc[t][rt][r]);
+                __builtin_fmaf(am[t][rt][r], sc[u][rt], yacc[t][rt][r]);
     }
   }
 
@@ -347,12 +363,18 @@ extern "C" int int4_gemv_bf16(const void* x, const uint32_t* w, const void* scal
   const auto* xb = static_cast<const uint16_t*>(x);
   const auto* sb = static_cast<const uint16_t*>(scale);
   if (m >= 2) {
-    const dim3 g2((unsigned)(((int64_t)n + kMfmaRows - 1) / kMfmaRows), (unsigned)tok_tiles);
+    // workgroups of 32 rows up to 32 tokens, of 64 rows beyond, where the
+    // activations re-read by every row block dominate
+    const int rows = m <= 32 ? 32 : 64;
+    const dim3 g2((unsigned)(((int64_t)n + rows - 1) / rows), (unsigned)tok_tiles);
     if (m <= 16)
-      hipLaunchKernelGGL((int4_gemm_mfma_kernel<1, 8>), g2, dim3(64 * 8), 0, s, xb, w, sb, m, n,
+      hipLaunchKernelGGL((int4_gemm_mfma_kernel<1, 8, 2>), g2, dim3(64 * 8), 0, s, xb, w, sb, m, n,
+                         k, y);
+    else if (m <= 32)
+      hipLaunchKernelGGL((int4_gemm_mfma_kernel<2, 4, 2>), g2, dim3(64 * 4), 0, s, xb, w, sb, m, n,
                          k, y);
     else
-      hipLaunchKernelGGL((int4_gemm_mfma_kernel<2, 4>), g2, dim3(64 * 4), 0, s, xb, w, sb, m, n,
+      hipLaunchKernelGGL((int4_gemm_mfma_kernel<2, 4, 4>), g2, dim3(64 * 4), 0, s, xb, w, sb, m, n,
                          k, y);
     return launch_status();
   }

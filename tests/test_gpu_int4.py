@@ -79,7 +79,7 @@ def _compare(got, ref, bound, what):
 # (tokens, rows, k)
 CASES = [(1, 16, 128), (1, 100, 384), (1, 21, 32768), (3, 37, 1024), (4, 64, 2048), (5, 33, 640),
          (8, 50, 8192), (13, 20, 256), (17, 7, 128), (2, 1, 1152), (40, 24, 256),
-         (64, 33, 512), (100, 9, 128), (16, 32, 4096)]
+         (64, 33, 512), (100, 9, 128), (16, 32, 4096), (32, 70, 256), (33, 200, 1024)]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"m{c[0]}_n{c[1]}_k{c[2]}")
