@@ -999,8 +999,8 @@ void attn_partial_kernel(AttnArgs a) {
   float* mg0 = reinterpret_cast<float*>(FP8 ? reinterpret_cast<char*>(lds) + kWaves * PB
                                             : reinterpret_cast<char*>(lds) + kWaves * PB + QB);
   constexpr int MS = (FP8 ? KB : partial_bytes<G>()) / 4;   // slot stride, floats
-  int* tmp = lds + (kWaves * (PB + KB) + QB + MB) / 4;   // kThreads + 1
-  int* pref = tmp + kThreads + 1;     // B + 1
+  int* tmp = lds + (kWaves * (PB + KB) + QB + MB) / 4;   // kWaves (the plan's wave totals)
+  int* pref = tmp + kWaves;           // B + 1
   int chunk;
   const int total_slots = build_plan(a, S, pref, tmp, chunk);
   // A work unit is kWaves consecutive chunk slots of one (sequence, kv
@@ -1378,7 +1378,10 @@ int attn_call(const pda_attn_shape* shape, const void* q, const void* k_cache,
   const size_t pbuf = (size_t)kWaves * ((size_t)(fp8 ? 1 : 2) * (size_t)G * 64 * 2 +
                                           (fp8 ? 8192 : 0)) +
                       (fp8 ? (size_t)G * kD * 2 : (size_t)kWaves * ((ib + 15) & ~(size_t)15));
-  const size_t lds = pbuf + (size_t)(kThreads + 1 + sh.num_seqs + 1) * sizeof(int);
+  // the plan's scan takes one int per wave; with B = 256 sequences the
+  // workgroup then fits four to a CU (40 KB each), which kThreads + 1 ints
+  // missed by 32 bytes
+  const size_t lds = pbuf + (size_t)(kWaves + sh.num_seqs + 1) * sizeof(int);
   // the per-sequence slot prefix lives in LDS too: past 64 KB (several
   // thousand sequences) the kernel needs the larger dynamic LDS limit
   if (!allow_lds(pk, lds)) return PDA_ERR_LAUNCH;
