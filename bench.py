@@ -4,10 +4,12 @@ MI355X, on the 64 sequences x 8192-token workload (64 query / 8 kv heads,
 head dim 128, pages of 16 tokens, FP8 e4m3 cache with per-head scales and 6 of
 128 K channels per kv head scaled by 20, split-K chunks of 512 tokens).
 
-A step = kv_write_fp8 of every sequence's newest token + validate_page_tags
-+ paged_decode_attn (split-K partials + combine), all on one stream with the
-inputs resident in HBM. The same step is timed with a BF16 cache built from
-the same bf16 inputs, for the FP8/BF16 ratio.
+A step = the kv write of every sequence's newest token and the page-tag
+check in one launch (kv_write_check) + paged_decode_attn (split-K partials +
+combine), all on one stream with the inputs resident in HBM; the same step
+with kv_write_fp8 and validate_page_tags as two launches is timed beside it.
+The same step is timed with a BF16 cache built from the same bf16 inputs,
+for the FP8/BF16 ratio.
 
 Prints one JSON line. `value` is algorithmic KV bytes per step / step time
 (GB/s). `roofline` rates the attention call (partial + combine kernels),
@@ -128,11 +130,24 @@ def breakdown(db, steps, torch):
         e[3].record()
         evs.append(e)
     torch.cuda.synchronize()
+    # the same with the write and the check in one launch (kv_write_check)
+    fev = []
+    for _ in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        db.write_check()
+        e[1].record()
+        db.attend()
+        e[2].record()
+        fev.append(e)
+    torch.cuda.synchronize()
     mean = lambda xs: sum(xs) / len(xs)
     return dict(kv_write_ms=mean([e[0].elapsed_time(e[1]) for e in evs]),
                 validate_ms=mean([e[1].elapsed_time(e[2]) for e in evs]),
                 attn_ms_with_events=mean([e[2].elapsed_time(e[3]) for e in evs]),
-                step_ms_with_call_events=mean([e[0].elapsed_time(e[3]) for e in evs]))
+                step_ms_with_call_events=mean([e[0].elapsed_time(e[3]) for e in evs]),
+                write_check_ms=mean([e[0].elapsed_time(e[1]) for e in fev]),
+                step_ms_fused_with_call_events=mean([e[0].elapsed_time(e[2]) for e in fev]))
 
 
 def pool_cycles(pool, seconds):
@@ -406,6 +421,7 @@ def full_pool_leg(args, torch, synth, pda, workload, overlap):
         db.step(overlap=overlap)
     t = interleaved_passes({"on": lambda: db.step(overlap=overlap),
                             "off": lambda: db.step(use_verdict=False),
+                            "two_launches": lambda: db.step(fused=False),
                             "attn": lambda: db.attend()}, args.steps, args.passes, torch)
     bd = breakdown(db, args.steps, torch)
     on, off, attn = median(t["on"]), median(t["off"]), median(t["attn"])
@@ -414,6 +430,9 @@ def full_pool_leg(args, torch, synth, pda, workload, overlap):
     out = {"workload": batch.cfg.name, "tokens": int(batch.seq_lens.sum()),
            "step_ms": on, "step_ms_no_op_tracker": off, "attn_ms": attn,
            "tag_check_overhead_frac": on / off - 1.0,
+           "step_ms_two_launches": median(t["two_launches"]),
+           "tag_check_overhead_frac_two_launches": median(t["two_launches"]) / off - 1.0,
+           "write_check_ms": bd["write_check_ms"],
            "validate_ms": bd["validate_ms"], "validate_frac_of_step":
                bd["validate_ms"] / bd["step_ms_with_call_events"],
            "kv_write_ms": bd["kv_write_ms"],
@@ -551,6 +570,7 @@ def main():
         "fp8_attn": lambda: fp8.attend(),
         "bf16_attn": lambda: bf.attend(),
         "fp8_step_no_op_tracker": lambda: fp8.step(use_verdict=False),
+        "fp8_step_two_launches": lambda: fp8.step(fused=False),
         "fp8_step_other_schedule": lambda: fp8.step(overlap=not overlap),
         "bf16_step_other_schedule": lambda: bf.step(overlap=not overlap),
     }, args.steps, args.passes, torch)
@@ -605,8 +625,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "64 seqs x 8192 ctx, 64 q / 8 kv heads, d128, page 16, "
                                "FP8 e4m3 KV (per-head scales; K 6/128 channels x20), "
-                               "split-K 512; step = kv write of 64 new tokens + tag "
-                               "validation + attention",
+                               "split-K 512; step = kv write of 64 new tokens and tag "
+                               "validation (one launch) + attention",
                    "global_batch": B, "seq_len": int(batch.seq_lens[0]),
                    "parallelism": "single GPU"},
         "timing": f"median of {args.passes} interleaved passes of exactly {args.steps} "
@@ -627,6 +647,10 @@ def main():
         "tag_check": {"step_ms_check_on": step8,
                       "step_ms_check_off": med["fp8_step_no_op_tracker"],
                       "overhead_frac": step8 / med["fp8_step_no_op_tracker"] - 1.0,
+                      "step_ms_two_launches": med["fp8_step_two_launches"],
+                      "overhead_frac_two_launches":
+                          med["fp8_step_two_launches"] / med["fp8_step_no_op_tracker"] - 1.0,
+                      "write_check_ms": bd8["write_check_ms"],
                       "tags_from": "libpda.so page pool (pda_pool_*), identical to the "
                                    "harness pool's bookkeeping"},
         "page_pool": time_page_pool(pda, np),

@@ -8,7 +8,7 @@ pointers. There is no CPU fallback: if the library or a GPU is missing the
 calls raise.
 
 Names follow the C ABI: kv_write_fp8, kv_write_bf16, validate_page_tags,
-paged_decode_attn_workspace_bytes, paged_decode_attn.
+kv_write_check, paged_decode_attn_workspace_bytes, paged_decode_attn.
 """
 from __future__ import annotations
 
@@ -24,6 +24,7 @@ KV_BF16, KV_FP8_E4M3 = 0, 1
 SCALE_NONE, SCALE_PER_HEAD, SCALE_PER_TOKEN = 0, 1, 2
 
 EXPORTS = ("kv_write_fp8", "kv_write_bf16", "kv_transcode_bf16_to_fp8", "validate_page_tags",
+           "kv_write_check",
            "paged_decode_attn_workspace_bytes", "paged_decode_attn",
            "paged_decode_attn_noalloc", "paged_decode_attn_noalloc_scratch_bytes",
            "pda_status_string", "pda_pool_create", "pda_pool_destroy", "pda_pool_alloc",
@@ -72,6 +73,9 @@ def load(path: str | None = None):
     lib.kv_transcode_bf16_to_fp8.restype = ctypes.c_int
     lib.validate_page_tags.argtypes = [V, I32, V, V, I32, V, I32, I32, V, V]
     lib.validate_page_tags.restype = ctypes.c_int
+    lib.kv_write_check.argtypes = [V, V, I64P, I32, I32, I32, I32, I32, I32, I32, I32, V, V, V,
+                                   V, V, V, V, V, I32, V, I32, V, V]
+    lib.kv_write_check.restype = ctypes.c_int
     lib.paged_decode_attn_workspace_bytes.argtypes = [ctypes.POINTER(AttnShape), I32]
     lib.paged_decode_attn_workspace_bytes.restype = ctypes.c_size_t
     lib.paged_decode_attn.argtypes = [ctypes.POINTER(AttnShape), V, V, V, V, V, V, V, I32,
@@ -193,6 +197,29 @@ def validate_page_tags(page_tags, block_table, expected_tags, seq_lens, verdict,
         _ptr(seq_lens, elem=4, name="seq_lens"), B, page_size,
         _ptr(verdict, elem=4, name="verdict"), _stream(stream))
     _check("validate_page_tags", st)
+
+
+def kv_write_check(k_new, v_new, slot_mapping, k_cache, v_cache, page_tags, block_table,
+                   expected_tags, seq_lens, verdict, *, page_size, num_pages, kv_dtype,
+                   scale_mode, k_scale=None, v_scale=None, token_scale=None, stream=None):
+    """kv_write_fp8 (kv_dtype KV_FP8_E4M3) or kv_write_bf16 (KV_BF16,
+    scale_mode SCALE_NONE) and validate_page_tags in one launch; arguments
+    as those calls take them."""
+    T, hkv, dk = k_new.shape
+    dv = v_new.shape[2] if v_new is not None else 0
+    B, max_blocks = block_table.shape
+    elem = 1 if kv_dtype == KV_FP8_E4M3 else 2
+    st = load().kv_write_check(
+        _ptr(k_new, elem=2, name="k_new"), _ptr(v_new, elem=2, name="v_new"),
+        _ptr(slot_mapping, elem=8, name="slot_mapping"), T, hkv, dk, dv, page_size, num_pages,
+        kv_dtype, scale_mode, _ptr(k_scale, elem=4, name="k_scale"),
+        _ptr(v_scale, elem=4, name="v_scale"), _ptr(token_scale, elem=4, name="token_scale"),
+        _ptr(k_cache, elem=elem, name="k_cache"), _ptr(v_cache, elem=elem, name="v_cache"),
+        _ptr(page_tags, elem=4, name="page_tags"), _ptr(block_table, elem=4, name="block_table"),
+        _ptr(expected_tags, elem=4, name="expected_tags"), max_blocks,
+        _ptr(seq_lens, elem=4, name="seq_lens"), B, _ptr(verdict, elem=4, name="verdict"),
+        _stream(stream))
+    _check("kv_write_check", st)
 
 
 def make_shape(*, num_seqs, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, page_size,

@@ -14,6 +14,7 @@
 // dims, which are contiguous in the K format and two bytes apart in the V
 // format (the V format interleaves the two tokens of a slot pair).
 #include "pda_internal.h"
+#include "validate_body.h"
 
 namespace pda {
 namespace {
@@ -74,16 +75,31 @@ __device__ __forceinline__ int64_t v_elem(int64_t page, int h, int off, int d, i
          (off & 1);
 }
 
+// Arguments of one kv write (FP8 or BF16 cache).
+struct WriteArgs {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int64_t* slots;
+  int hkv, dk, dv, S, P;
+  const float* k_scale;
+  const float* v_scale;
+  float* token_scale;
+  void* k_cache;
+  void* v_cache;
+};
+
+// Token t of an FP8 write, by one workgroup of kThreads threads; red is
+// kThreads / 64 floats of LDS.
 template <bool PER_TOKEN>
-__global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(
-    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    const int64_t* __restrict__ slots, int hkv, int dk, int dv, int S, int P,
-    const float* __restrict__ k_scale, const float* __restrict__ v_scale,
-    float* __restrict__ token_scale, uint8_t* __restrict__ k_cache,
-    uint8_t* __restrict__ v_cache) {
-  __shared__ float red[kThreads / 64];
-  const int t = blockIdx.x;
-  const int64_t slot = slots[t];
+__device__ __forceinline__ void write_token_fp8(const WriteArgs& w, int t, float* red) {
+  const uint16_t* __restrict__ k_new = w.k_new;
+  const uint16_t* __restrict__ v_new = w.v_new;
+  const int hkv = w.hkv, dk = w.dk, dv = w.dv, S = w.S, P = w.P;
+  const float* __restrict__ k_scale = w.k_scale;
+  const float* __restrict__ v_scale = w.v_scale;
+  uint8_t* __restrict__ k_cache = static_cast<uint8_t*>(w.k_cache);
+  uint8_t* __restrict__ v_cache = static_cast<uint8_t*>(w.v_cache);
+  const int64_t slot = w.slots[t];
   if (slot < 0 || slot >= (int64_t)P * S) return;
   const int64_t page = slot / S;
   const int off = (int)(slot % S);
@@ -101,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(
     __syncthreads();
     amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     tok_sc = (amax > 0.0f) ? amax / 448.0f : 1.0f;
-    if (tid == 0) token_scale[slot] = tok_sc;
+    if (tid == 0) w.token_scale[slot] = tok_sc;
   }
 
   // K: groups of 4 dims, contiguous in the cache.
@@ -133,12 +149,14 @@ __global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(
   }
 }
 
-__global__ __launch_bounds__(kThreads) void kv_write_bf16_kernel(
-    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    const int64_t* __restrict__ slots, int hkv, int dk, int dv, int S, int P,
-    uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache) {
-  const int t = blockIdx.x;
-  const int64_t slot = slots[t];
+// Token t of a BF16 write (a copy into the cache formats).
+__device__ __forceinline__ void write_token_bf16(const WriteArgs& w, int t) {
+  const uint16_t* __restrict__ k_new = w.k_new;
+  const uint16_t* __restrict__ v_new = w.v_new;
+  const int hkv = w.hkv, dk = w.dk, dv = w.dv, S = w.S, P = w.P;
+  uint16_t* __restrict__ k_cache = static_cast<uint16_t*>(w.k_cache);
+  uint16_t* __restrict__ v_cache = static_cast<uint16_t*>(w.v_cache);
+  const int64_t slot = w.slots[t];
   if (slot < 0 || slot >= (int64_t)P * S) return;
   const int64_t page = slot / S;
   const int off = (int)(slot % S);
@@ -216,6 +234,51 @@ __device__ __forceinline__ bool pair_ok(int src, int dst, int n, int ps, int pd,
 // are contiguous (Hkv*S*Dk K elements, then Hkv*S*Dv V elements), each
 // thread takes 8 elements per step, four steps' loads issued before their
 // conversions and stores.
+template <bool PER_TOKEN>
+__global__ __launch_bounds__(kThreads) void kv_write_fp8_kernel(WriteArgs w) {
+  __shared__ float red[kThreads / 64];
+  write_token_fp8<PER_TOKEN>(w, blockIdx.x, red);
+}
+
+__global__ __launch_bounds__(kThreads) void kv_write_bf16_kernel(WriteArgs w) {
+  write_token_bf16(w, blockIdx.x);
+}
+
+// Arguments of one page-tag check.
+struct CheckArgs {
+  const uint32_t* page_tags;
+  int P;
+  const int32_t* block_table;
+  const uint32_t* expected;
+  int max_blocks;
+  const int32_t* lens;
+  int S;
+  int32_t* verdict;
+};
+
+// The kv write and the page-tag check of one decode step in one launch:
+// workgroups [0, T) write token t, workgroups [T, T + B) check sequence
+// t - T. The two touch disjoint memory (the check reads tags, table and
+// lengths and writes verdicts; the write reads new rows and writes cache
+// bytes), so their order does not matter, and the launch boundary orders
+// both before the attention that follows. MODE 0: FP8 per-head scales, 1:
+// FP8 per-token scales, 2: BF16.
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void kv_write_check_kernel(WriteArgs w, int T,
+                                                                  CheckArgs c) {
+  static_assert(kThreads == kValidateThreads, "one workgroup shape for both parts");
+  __shared__ float red[kThreads / 64];
+  __shared__ int best[kThreads / 64];
+  const int b = blockIdx.x;
+  if (b < T) {
+    if constexpr (MODE == 2) write_token_bf16(w, b);
+    else write_token_fp8<MODE == 1>(w, b, red);
+  } else {
+    validate_seq(b - T, c.page_tags, c.P, c.block_table, c.expected, c.max_blocks, c.lens, c.S,
+                 c.verdict, best);
+  }
+}
+
 template <bool V, bool FAST>
 __device__ __forceinline__ void transcode_span(const uint16_t* __restrict__ src,
                                                uint8_t* __restrict__ dst, int n_elems,
@@ -403,14 +466,12 @@ extern "C" int kv_write_fp8(const void* k_new, const void* v_new, const int64_t*
   hipStream_t s = as_stream(stream);
   const auto* kn = static_cast<const uint16_t*>(k_new);
   const auto* vn = static_cast<const uint16_t*>(v_new);
+  const WriteArgs w{kn, vn, slot_mapping, num_kv_heads, head_dim_k, head_dim_v, page_size,
+                   num_pages, k_scale, v_scale, token_scale, k_cache, v_cache};
   if (scale_mode == PDA_SCALE_PER_TOKEN)
-    hipLaunchKernelGGL(kv_write_fp8_kernel<true>, dim3(num_tokens), dim3(kThreads), 0, s, kn,
-                       vn, slot_mapping, num_kv_heads, head_dim_k, head_dim_v, page_size,
-                       num_pages, k_scale, v_scale, token_scale, k_cache, v_cache);
+    hipLaunchKernelGGL(kv_write_fp8_kernel<true>, dim3(num_tokens), dim3(kThreads), 0, s, w);
   else
-    hipLaunchKernelGGL(kv_write_fp8_kernel<false>, dim3(num_tokens), dim3(kThreads), 0, s, kn,
-                       vn, slot_mapping, num_kv_heads, head_dim_k, head_dim_v, page_size,
-                       num_pages, k_scale, v_scale, token_scale, k_cache, v_cache);
+    hipLaunchKernelGGL(kv_write_fp8_kernel<false>, dim3(num_tokens), dim3(kThreads), 0, s, w);
   return launch_status();
 }
 
@@ -422,11 +483,72 @@ extern "C" int kv_write_bf16(const void* k_new, const void* v_new, const int64_t
                         head_dim_v, page_size, num_pages, k_cache, v_cache);
   if (st != PDA_OK) return st;
   if (num_tokens == 0) return PDA_OK;
+  const WriteArgs w{static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                   slot_mapping, num_kv_heads, head_dim_k, head_dim_v, page_size, num_pages,
+                   nullptr, nullptr, nullptr, k_cache, v_cache};
   hipLaunchKernelGGL(kv_write_bf16_kernel, dim3(num_tokens), dim3(kThreads), 0,
-                     as_stream(stream), static_cast<const uint16_t*>(k_new),
-                     static_cast<const uint16_t*>(v_new), slot_mapping, num_kv_heads, head_dim_k,
-                     head_dim_v, page_size, num_pages, static_cast<uint16_t*>(k_cache),
-                     static_cast<uint16_t*>(v_cache));
+                     as_stream(stream), w);
+  return launch_status();
+}
+
+extern "C" int kv_write_check(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                              int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim_k,
+                              int32_t head_dim_v, int32_t page_size, int32_t num_pages,
+                              int32_t kv_dtype, int32_t scale_mode, const float* k_scale,
+                              const float* v_scale, float* token_scale, void* k_cache,
+                              void* v_cache, const uint32_t* page_tags,
+                              const int32_t* block_table, const uint32_t* expected_tags,
+                              int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                              int32_t num_seqs, int32_t* verdict, void* stream) {
+  // the write's arguments, as kv_write_fp8 / kv_write_bf16 check them (not
+  // read at all when there are no tokens: empty tensors may come as NULL)
+  int mode = 0;
+  if (num_tokens < 0) return PDA_ERR_INVALID_ARG;
+  if (num_tokens > 0) {
+    int st = check_common(k_new, v_new, slot_mapping, num_tokens, num_kv_heads, head_dim_k,
+                          head_dim_v, page_size, num_pages, k_cache, v_cache);
+    if (st != PDA_OK) return st;
+    const bool latent = (v_new == nullptr);
+    if (kv_dtype == PDA_KV_FP8_E4M3) {
+      if (scale_mode == PDA_SCALE_PER_HEAD) {
+        if (!k_scale || (!latent && !v_scale) || token_scale) return PDA_ERR_INVALID_ARG;
+        mode = 0;
+      } else if (scale_mode == PDA_SCALE_PER_TOKEN) {
+        if (!token_scale || k_scale || v_scale) return PDA_ERR_INVALID_ARG;
+        if (!latent || num_kv_heads != 1) return PDA_ERR_UNSUPPORTED;
+        mode = 1;
+      } else {
+        return PDA_ERR_INVALID_ARG;
+      }
+    } else if (kv_dtype == PDA_KV_BF16) {
+      if (scale_mode != PDA_SCALE_NONE || k_scale || v_scale || token_scale)
+        return PDA_ERR_INVALID_ARG;
+      mode = 2;
+    } else {
+      return PDA_ERR_INVALID_ARG;
+    }
+  }
+  // the check's arguments, as validate_page_tags checks them
+  if (num_seqs < 0) return PDA_ERR_INVALID_ARG;
+  if (num_seqs > 0 && (max_blocks_per_seq <= 0 || num_pages <= 0 || page_size <= 0))
+    return PDA_ERR_INVALID_ARG;
+  if (num_seqs > 0 && (!page_tags || !block_table || !expected_tags || !seq_lens || !verdict))
+    return PDA_ERR_INVALID_ARG;
+  if ((int64_t)num_tokens + num_seqs > 0x7FFFFFFF) return PDA_ERR_UNSUPPORTED;
+  if (num_tokens + num_seqs == 0) return PDA_OK;
+  const WriteArgs w{static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                    slot_mapping, num_kv_heads, head_dim_k, head_dim_v, page_size, num_pages,
+                    k_scale, v_scale, token_scale, k_cache, v_cache};
+  const CheckArgs c{page_tags, num_pages, block_table, expected_tags, max_blocks_per_seq,
+                    seq_lens, page_size, verdict};
+  const dim3 grid((unsigned)(num_tokens + num_seqs));
+  hipStream_t s = as_stream(stream);
+  if (mode == 0)
+    hipLaunchKernelGGL(kv_write_check_kernel<0>, grid, dim3(kThreads), 0, s, w, num_tokens, c);
+  else if (mode == 1)
+    hipLaunchKernelGGL(kv_write_check_kernel<1>, grid, dim3(kThreads), 0, s, w, num_tokens, c);
+  else
+    hipLaunchKernelGGL(kv_write_check_kernel<2>, grid, dim3(kThreads), 0, s, w, num_tokens, c);
   return launch_status();
 }
 

@@ -28,7 +28,8 @@
  *  - Re-entrant; no global mutable state beyond a per-device cache of the
  *    compute-unit count.
  *  - Intended order on one stream per decode step:
- *        kv_write_fp8 -> validate_page_tags -> paged_decode_attn.
+ *        kv_write_fp8 -> validate_page_tags -> paged_decode_attn,
+ *    or kv_write_check (the first two in one launch) -> paged_decode_attn.
  *
  * Physical KV-cache format ("page" = `page_size` consecutive token slots of
  * one sequence; slot = page * page_size + offset). Element size is 1 byte for
@@ -147,6 +148,44 @@ int kv_write_bf16(const void* k_new, const void* v_new,
                   int32_t num_kv_heads, int32_t head_dim_k, int32_t head_dim_v,
                   int32_t page_size, int32_t num_pages,
                   void* k_cache, void* v_cache, void* stream);
+
+/*
+ * kv_write_check — the kv write and the page-tag check of one decode step in
+ * a single launch: exactly the effect of kv_write_fp8 (kv_dtype
+ * PDA_KV_FP8_E4M3) or kv_write_bf16 (PDA_KV_BF16, scale_mode PDA_SCALE_NONE,
+ * all scale pointers NULL) followed by validate_page_tags on the same
+ * stream, with the arguments of both (num_pages and page_size serve both).
+ * The check stays a batch step of its own, outside attention, as the pages
+ * describe it ([SK] § "Kvalita odpovedí a integrita spoločnej cache"; [DE]
+ * § "Sicherheit gemeinsamer KV-Caches wird zum Produktionsthema"); it only
+ * shares the launch with the write, which it does not depend on: the write
+ * changes cache bytes, the check reads tags, the block table and lengths.
+ * Workgroups [0, num_tokens) write one token each and workgroups
+ * [num_tokens, num_tokens + num_seqs) check one sequence each, so the
+ * launch costs one kernel start instead of two.
+ *
+ *  Write arguments as kv_write_fp8 / kv_write_bf16 (k_cache and v_cache
+ *  point at uint8 codes or uint16 BF16 elements); check arguments as
+ *  validate_page_tags. num_tokens == 0 runs the check alone and reads
+ *  none of the write's arguments (empty inputs may be NULL); num_seqs == 0
+ *  runs the write alone and reads none of the check's pointers; both zero
+ *  is a no-op.
+ *  The caches must not overlap page_tags, block_table, expected_tags,
+ *  seq_lens or verdict.
+ *  Errors: those of the two calls it replaces; PDA_ERR_INVALID_ARG for an
+ *  unknown kv_dtype; PDA_ERR_UNSUPPORTED when num_tokens + num_seqs exceeds
+ *  2^31 - 1.
+ */
+int kv_write_check(const void* k_new, const void* v_new,
+                   const int64_t* slot_mapping, int32_t num_tokens,
+                   int32_t num_kv_heads, int32_t head_dim_k, int32_t head_dim_v,
+                   int32_t page_size, int32_t num_pages, int32_t kv_dtype,
+                   int32_t scale_mode, const float* k_scale,
+                   const float* v_scale, float* token_scale, void* k_cache,
+                   void* v_cache, const uint32_t* page_tags,
+                   const int32_t* block_table, const uint32_t* expected_tags,
+                   int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                   int32_t num_seqs, int32_t* verdict, void* stream);
 
 /*
  * kv_transcode_bf16_to_fp8 — re-encode pages of a BF16 cache as pages of an

@@ -18,7 +18,7 @@ import numpy as np
 import synth
 from decode_attention_fp8_write_amd import (
     KV_BF16, KV_FP8_E4M3, SCALE_NONE, SCALE_PER_HEAD, SCALE_PER_TOKEN, kv_write_bf16,
-    kv_write_fp8, make_shape, paged_decode_attn, paged_decode_attn_workspace_bytes,
+    kv_write_check, kv_write_fp8, make_shape, paged_decode_attn, paged_decode_attn_workspace_bytes,
     validate_page_tags)
 
 
@@ -99,6 +99,25 @@ class DeviceBatch:
             kv_write_bf16(self.step_k, self.step_v, self.step_slots, self.k_cache,
                           self.v_cache, page_size=S, num_pages=P, stream=stream)
 
+    def write_check(self, stream=None):
+        """write_step and validate in one launch (kv_write_check)."""
+        S, P = self.cfg.page_size, self.batch.num_pages
+        if self.step_k is None:
+            self.validate(stream)
+            return
+        fp8 = self.kv_dtype == KV_FP8_E4M3
+        if fp8 and self.cfg.v_in_k:
+            kw = dict(scale_mode=SCALE_PER_TOKEN, token_scale=self.k_scale)
+        elif fp8:
+            kw = dict(scale_mode=SCALE_PER_HEAD, k_scale=self.k_scale, v_scale=self.v_scale)
+        else:
+            kw = dict(scale_mode=SCALE_NONE)
+        kv_write_check(self.step_k, None if self.cfg.v_in_k else self.step_v, self.step_slots,
+                       self.k_cache, None if self.cfg.v_in_k else self.v_cache,
+                       self.page_tags, self.block_table, self.expected_tags, self.seq_lens,
+                       self.verdict, page_size=S, num_pages=P, kv_dtype=self.kv_dtype,
+                       stream=stream, **kw)
+
     def validate(self, stream=None):
         validate_page_tags(self.page_tags, self.block_table, self.expected_tags,
                            self.seq_lens, self.verdict, page_size=self.cfg.page_size,
@@ -115,15 +134,21 @@ class DeviceBatch:
                           self.verdict if use_verdict else None, self.workspace, self.out,
                           stream=stream)
 
-    def step(self, use_verdict: bool = True, stream=None, overlap: bool = False):
+    def step(self, use_verdict: bool = True, stream=None, overlap: bool = False,
+             fused: bool = True):
         """One decode step: kv write of the newest tokens, the tag check,
-        attention. overlap: the tag check runs on a second stream (default
-        priority) beside the kv write, which it does not depend on; attention
-        waits for both."""
+        attention. fused: the write and the check share one launch
+        (kv_write_check); otherwise they are two launches in a row.
+        overlap: the tag check runs on a second stream (default priority)
+        beside the kv write, which it does not depend on; attention waits for
+        both."""
         if not (overlap and use_verdict):
-            self.write_step(stream)
-            if use_verdict:
-                self.validate(stream)
+            if use_verdict and fused:
+                self.write_check(stream)
+            else:
+                self.write_step(stream)
+                if use_verdict:
+                    self.validate(stream)
             self.attend(use_verdict, stream)
             return
         import torch

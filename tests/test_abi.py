@@ -30,6 +30,7 @@ def pda():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     assert names == sorted(["kv_write_fp8", "kv_write_bf16", "kv_transcode_bf16_to_fp8",
+                            "kv_write_check",
                             "pda_pool_create", "pda_pool_destroy", "pda_pool_alloc",
                             "pda_pool_free", "pda_pool_tags", "pda_pool_num_free",
                             "pda_hbm_read_probe", "pda_hbm_read_probe_sink_words",
@@ -133,6 +134,35 @@ def test_argument_checks_return_before_launch(pda):
         pda.PDA_ERR_INVALID_ARG
     assert lib.validate_page_tags(null, 64, fake, fake, 16, fake, 4, 16, fake, null) == \
         pda.PDA_ERR_INVALID_ARG
+
+
+def test_write_check_argument_checks(pda):
+    """kv_write_check refuses what either call it replaces refuses, before
+    anything is launched."""
+    lib = pda.load()
+    null = None
+    fake = ctypes.c_void_p(256)
+
+    def call(T=4, dtype=None, mode=None, ks=fake, vs=fake, ts=null, tags=fake, B=4, ver=fake,
+             mb=16, dk=128):
+        dtype = pda.KV_FP8_E4M3 if dtype is None else dtype
+        mode = pda.SCALE_PER_HEAD if mode is None else mode
+        return lib.kv_write_check(fake, fake, fake, T, 8, dk, 128, 16, 64, dtype, mode, ks, vs,
+                                  ts, fake, fake, tags, fake, fake, mb, fake, B, ver, null)
+
+    assert call(dtype=7) == pda.PDA_ERR_INVALID_ARG                 # unknown cache dtype
+    assert call(mode=7) == pda.PDA_ERR_INVALID_ARG                  # unknown scale mode
+    assert call(dtype=pda.KV_BF16) == pda.PDA_ERR_INVALID_ARG       # BF16 takes no scales
+    assert call(mode=pda.SCALE_PER_TOKEN, ks=null, vs=null, ts=fake) == pda.PDA_ERR_UNSUPPORTED
+    assert call(dk=100) == pda.PDA_ERR_UNSUPPORTED                  # the write's shape rules
+    assert call(T=-1) == pda.PDA_ERR_INVALID_ARG
+    assert call(B=-1) == pda.PDA_ERR_INVALID_ARG                    # the check's sizes
+    assert call(mb=0) == pda.PDA_ERR_INVALID_ARG
+    assert call(tags=null) == pda.PDA_ERR_INVALID_ARG               # the check's pointers
+    assert call(ver=null) == pda.PDA_ERR_INVALID_ARG
+    # nothing to do: a no-op; sequences only need no write pointers checked
+    assert call(T=0, B=0) == pda.PDA_OK
+    assert call(B=0, tags=null, ver=null, T=0) == pda.PDA_OK
 
 
 def test_transcode_argument_checks(pda):
