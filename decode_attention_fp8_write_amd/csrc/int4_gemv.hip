@@ -195,10 +195,12 @@ __global__ __launch_bounds__(64 * kWaves) void int4_gemv_kernel(
 // tokens run side by side and share the weights through the caches); its NW
 // waves take every NW-th scale group and meet in LDS at the end: eight waves
 // for one 16-token tile, four for two, whose registers leave room for fewer
-// waves (measured: eight waves 3-4 us faster up to 16 tokens, even at 32,
-// slower at 64). Every row block re-reads the activations, from L2: two row
-// tiles serve up to 32 tokens, four beyond (8192 x 8192, 64 tokens: 36.5 us
-// against 47.4 us with two; 32 tokens: 36.2 against 26.8; eight tiles 55 us).
+// waves. Every row block re-reads the activations, from L2, through LDS
+// (below): two row tiles serve up to 32 tokens, four beyond (8192 x 8192,
+// measured over 16-, 32-, 64- and 128-row and 16- and 32-token tiles with
+// four and eight waves: 64 tokens 29.2 us with four row tiles against 31.5
+// with two and 50.8 with eight; 32 tokens 20.2 with two against 28.6 with
+// four; up to 16 tokens the 16-token, 32-row, eight-wave form is fastest).
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -209,7 +211,22 @@ template <int TILES, int NW, int kRT>
 __global__ __launch_bounds__(64 * NW) void int4_gemm_mfma_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ w,
     const uint16_t* __restrict__ scale, int m, int n, int k, float* __restrict__ y) {
-  __shared__ float red[NW - 1][TILES * kRT * 4][64];
+  // U groups per wave and step, their loads issued before any use
+  constexpr int U = 2;
+  // Activations go through LDS: each wave copies the tiles of its U groups
+  // (16 tokens x 128 inputs, 256 bytes a token) with direct global->LDS
+  // copies, a copy taking four tokens' contiguous 256 bytes, and reads the
+  // matrix-core operands back from there. (Loaded straight into the operand
+  // layout, each load touched sixteen tokens' rows.) In the tile, token c's
+  // 16-byte chunk j sits at position (j + c) mod 16 of its 256 bytes, so the
+  // sixteen tokens one operand read touches hit sixteen different bank
+  // quads. The final reduction reuses the same memory.
+  constexpr int kTileB = 16 * 256;
+  constexpr int kXsB = NW * U * TILES * kTileB;
+  static_assert(kXsB <= 65536, "activation tiles fit the static LDS");
+  static_assert((NW - 1) * TILES * kRT * 4 * 64 * 4 <= kXsB, "reduction fits the tiles");
+  __shared__ __attribute__((aligned(16))) uint8_t xs_all[kXsB];
+  float (*red)[TILES * kRT * 4][64] = reinterpret_cast<float (*)[TILES * kRT * 4][64]>(xs_all);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -226,10 +243,23 @@ __global__ __launch_bounds__(64 * NW) void int4_gemm_mfma_kernel(
     wr[rt] = w + (int64_t)row * (k / 8) + 4 * g;
     sr[rt] = scale + (int64_t)row * groups;
   }
-  const uint16_t* xr[TILES];
+  uint8_t* const xs = xs_all + wave * (U * TILES * kTileB);
+  const uint32_t xs_lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)xs));
+  // copy i of tile t: lane L writes position L & 15 of token 4i + (L >> 4)
+  // of the tile, i.e. chunk ((L & 15) - token) mod 16 of that token
+  auto copy_tile = [&](int gi, int slot, int t) {
 #pragma unroll
-  for (int t = 0; t < TILES; ++t)
-    xr[t] = x + (int64_t)min(tok0 + 16 * t + c, m - 1) * k + 32 * g;
+    for (int i = 0; i < 4; ++i) {
+      const int tt = 4 * i + (lane >> 4);
+      const int j = ((lane & 15) - tt) & 15;
+      const int tok = min(tok0 + 16 * t + tt, m - 1);
+      const uint64_t ga = (uint64_t)(uintptr_t)(x + (int64_t)tok * k + kGroup * gi + 8 * j);
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                   :: "s"(xs_lds + (uint32_t)((slot * TILES + t) * kTileB + i * 1024)), "v"(ga)
+                   : "memory");
+    }
+  };
 
   const uint4 cn136 = make_uint4(kNeg136, kNeg136, kNeg136, kNeg136);
   const bf16x8_t bneg136 = __builtin_bit_cast(bf16x8_t, cn136);
@@ -239,12 +269,20 @@ __global__ __launch_bounds__(64 * NW) void int4_gemm_mfma_kernel(
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) yacc[t][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // U groups per wave and step, their loads issued before any use
-  constexpr int U = TILES == 1 ? 4 : 2;
   for (int g0 = wave; g0 < groups; g0 += NW * U) {
     uint4 wv[U][kRT];
     float sc[U][kRT];
-    uint4 xv[U][TILES][4];
+    // the copies first: the compiler's waits for the weight loads below
+    // then also cover them (loads complete in order), and the explicit wait
+    // after the loads covers them in any case
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int gi = g0 + NW * u;
+      if (gi < groups) {
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) copy_tile(gi, u, t);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int gi = g0 + NW * u;
@@ -254,13 +292,9 @@ __global__ __launch_bounds__(64 * NW) void int4_gemm_mfma_kernel(
           wv[u][rt] = *reinterpret_cast<const uint4*>(wr[rt] + 16 * gi);
           sc[u][rt] = bf16_bits_to_f32(sr[rt][gi]);
         }
-#pragma unroll
-        for (int t = 0; t < TILES; ++t)
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            xv[u][t][s] = *reinterpret_cast<const uint4*>(xr[t] + kGroup * gi + 8 * s);
       }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (g0 + NW * u >= groups) break;
@@ -273,7 +307,9 @@ __global__ __launch_bounds__(64 * NW) void int4_gemm_mfma_kernel(
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           uint32_t p[4];
-          pair_up(xv[u][t][s], p);
+          const uint4 xv = *reinterpret_cast<const uint4*>(
+              xs + (u * TILES + t) * kTileB + c * 256 + (((4 * g + s + c) & 15) * 16));
+          pair_up(xv, p);
           av[t][s] = __builtin_bit_cast(bf16x8_t, make_uint4(p[0], p[1], p[2], p[3]));
         }
         nac[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -312,7 +348,9 @@ __global__ __launch_bounds__(64 * NW) void int4_gemm_mfma_kernel(
     }
   }
 
-  // the other waves hand their partial sums to wave 0
+  // the other waves hand their partial sums to wave 0, through the memory
+  // the tiles used (every wave is done with its tiles past this barrier)
+  __syncthreads();
   if (wave > 0) {
 #pragma unroll
     for (int t = 0; t < TILES; ++t)
