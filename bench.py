@@ -22,7 +22,9 @@ on a bounded sample of the same workload on the host cores.
 Every timed figure is the median over N interleaved passes of exactly K
 calls between two HIP events on the launch stream (FP8 and BF16 steps, the
 attention calls alone, and the no-op-tracker step alternate within each
-pass), after W warm-up steps. Extra keys: the latent workload's attention
+pass), after W warm-up steps. The tag check's share of the step is the
+median over the passes of the ratio of the step with the check to the step
+with the no-op tracker timed right after it. Extra keys: the latent workload's attention
 call against the matrix-core peak, the full-pool workload's step with the
 tag check's share, the BF16 -> FP8 page transcode, the INT4 GEMV.
 """
@@ -429,9 +431,10 @@ def full_pool_leg(args, torch, synth, pda, workload, overlap):
     log(f"full pool: step {on:.4f} ms (no-op tracker {off:.4f}), attention {attn:.4f} ms")
     out = {"workload": batch.cfg.name, "tokens": int(batch.seq_lens.sum()),
            "step_ms": on, "step_ms_no_op_tracker": off, "attn_ms": attn,
-           "tag_check_overhead_frac": on / off - 1.0,
+           "tag_check_overhead_frac": median([a / b for a, b in zip(t["on"], t["off"])]) - 1.0,
            "step_ms_two_launches": median(t["two_launches"]),
-           "tag_check_overhead_frac_two_launches": median(t["two_launches"]) / off - 1.0,
+           "tag_check_overhead_frac_two_launches":
+               median([a / b for a, b in zip(t["two_launches"], t["off"])]) - 1.0,
            "write_check_ms": bd["write_check_ms"],
            "validate_ms": bd["validate_ms"], "validate_frac_of_step":
                bd["validate_ms"] / bd["step_ms_with_call_events"],
@@ -564,13 +567,16 @@ def main():
         fp8.step(overlap=overlap)
         bf.step(overlap=overlap)
     log(f"timing {args.passes} interleaved passes of {args.steps} steps ({args.schedule})")
+    # the step with and without the check run next to each other in every
+    # round, so that the check's share is taken pass by pass (drift between
+    # legs further apart in a round was as large as the check itself)
     t = interleaved_passes({
         "fp8_step": lambda: fp8.step(overlap=overlap),
+        "fp8_step_no_op_tracker": lambda: fp8.step(use_verdict=False),
+        "fp8_step_two_launches": lambda: fp8.step(fused=False),
         "bf16_step": lambda: bf.step(overlap=overlap),
         "fp8_attn": lambda: fp8.attend(),
         "bf16_attn": lambda: bf.attend(),
-        "fp8_step_no_op_tracker": lambda: fp8.step(use_verdict=False),
-        "fp8_step_two_launches": lambda: fp8.step(fused=False),
         "fp8_step_other_schedule": lambda: fp8.step(overlap=not overlap),
         "bf16_step_other_schedule": lambda: bf.step(overlap=not overlap),
     }, args.steps, args.passes, torch)
@@ -646,10 +652,12 @@ def main():
         "step_ms_with_call_events": bd8["step_ms_with_call_events"],
         "tag_check": {"step_ms_check_on": step8,
                       "step_ms_check_off": med["fp8_step_no_op_tracker"],
-                      "overhead_frac": step8 / med["fp8_step_no_op_tracker"] - 1.0,
+                      "overhead_frac": median([a / b for a, b in zip(
+                          t["fp8_step"], t["fp8_step_no_op_tracker"])]) - 1.0,
+                      "overhead_frac_of_medians": step8 / med["fp8_step_no_op_tracker"] - 1.0,
                       "step_ms_two_launches": med["fp8_step_two_launches"],
-                      "overhead_frac_two_launches":
-                          med["fp8_step_two_launches"] / med["fp8_step_no_op_tracker"] - 1.0,
+                      "overhead_frac_two_launches": median([a / b for a, b in zip(
+                          t["fp8_step_two_launches"], t["fp8_step_no_op_tracker"])]) - 1.0,
                       "write_check_ms": bd8["write_check_ms"],
                       "tags_from": "libpda.so page pool (pda_pool_*), identical to the "
                                    "harness pool's bookkeeping"},
