@@ -105,12 +105,6 @@ __device__ __forceinline__ int n_chunks_of(const AttnArgs& a, int s, int S, int 
   return (len + chunk - 1) / chunk;
 }
 
-// Chunk slots of a sequence: its chunk count rounded up to a multiple of the
-// waves of a workgroup (one work unit = kWaves consecutive chunks of one
-// (sequence, kv head), one per wave).
-__device__ __forceinline__ int n_slots_of(const AttnArgs& a, int s, int S, int chunk) {
-  return (n_chunks_of(a, s, S, chunk) + kWaves - 1) / kWaves * kWaves;
-}
 
 // Every workgroup derives the same plan: chunk size (doubled until the
 // unit partials fit the workspace) and the exclusive prefix of chunk slots per
@@ -123,9 +117,27 @@ __device__ int build_plan(const AttnArgs& a, int S, int* pref, int* tmp, int& ch
   const int lane = tid & 63, wave = tid >> 6;
   int chunk = a.chunk0;
   int total = 0;
+  // Each sequence's length and verdict are loaded together, once, and the
+  // length it contributes (0 if aborted or malformed) is parked in pref[s]
+  // until the scan overwrites it (loaded on demand, every count of the plan
+  // took two dependent round trips, twice over: 4.5 us of every workgroup's
+  // start). A retry with a doubled chunk loads them again.
+  for (int s = beg; s < end; ++s) {
+    const int len = a.lens[s];
+    const int ver = a.verdict != nullptr ? a.verdict[s] : 0;
+    pref[s] = (len <= 0 || len > a.max_blocks * S || ver != 0) ? 0 : len;
+  }
+  bool parked = true;
+  // chunk slots of a sequence: its chunk count rounded up to a multiple of
+  // the waves of a workgroup (one work unit = kWaves consecutive chunks of
+  // one (sequence, kv head), one per wave)
+  auto slots = [&](int s) -> int {
+    const int len = parked ? pref[s] : (n_chunks_of(a, s, S, 1) > 0 ? a.lens[s] : 0);
+    return ((len + chunk - 1) / chunk + kWaves - 1) / kWaves * kWaves;
+  };
   for (;;) {
     int local = 0;
-    for (int s = beg; s < end; ++s) local += n_slots_of(a, s, S, chunk);
+    for (int s = beg; s < end; ++s) local += slots(s);
     // exclusive prefix of `local` over the workgroup: an inclusive scan
     // within each wave, then the totals of the waves before this one
     int v = local;
@@ -145,9 +157,11 @@ __device__ int build_plan(const AttnArgs& a, int S, int* pref, int* tmp, int& ch
       total += t;
     }
     for (int s = beg; s < end; ++s) {
+      const int n = slots(s);
       pref[s] = run;
-      run += n_slots_of(a, s, S, chunk);
+      run += n;
     }
+    parked = false;
     __syncthreads();
     if ((long long)(total / kWaves) * a.Hkv <= a.cap_items) break;
     chunk *= 2;

@@ -111,13 +111,6 @@ struct LatArgs {
   float sm_scale;
 };
 
-__device__ __forceinline__ int seq_pages(const LatArgs& a, int s) {
-  const int len = a.lens[s];
-  if (len <= 0 || len > a.max_blocks * kS) return 0;
-  if (a.verdict != nullptr && a.verdict[s] != 0) return 0;
-  return (len + kS - 1) / kS;
-}
-
 // Workgroup owning global page g when T pages are cut into W ranges
 // [floor(wT/W), floor((w+1)T/W)).
 __device__ __forceinline__ int owner_of(long long g, long long T, long long W) {
@@ -276,8 +269,16 @@ void latent_partial_kernel(LatArgs a) {
     const int per = (a.B + NT - 1) / NT;
     const int beg = min(a.B, tid * per);
     const int end = min(a.B, beg + per);
+    // each sequence's page count once (its length and verdict loaded
+    // together), parked in pref[s] until the scan below overwrites it
     int local = 0;
-    for (int s = beg; s < end; ++s) local += seq_pages(a, s);
+    for (int s = beg; s < end; ++s) {
+      const int len = a.lens[s];
+      const int ver = a.verdict != nullptr ? a.verdict[s] : 0;
+      const int np = (len <= 0 || len > a.max_blocks * kS || ver != 0) ? 0 : (len + kS - 1) / kS;
+      pref[s] = np;
+      local += np;
+    }
     tmp[tid] = local;
     __syncthreads();
     if (tid == 0) {
@@ -292,8 +293,9 @@ void latent_partial_kernel(LatArgs a) {
     __syncthreads();
     int run = tmp[tid];
     for (int s = beg; s < end; ++s) {
+      const int np = pref[s];
       pref[s] = run;
-      run += seq_pages(a, s);
+      run += np;
     }
     const int total = tmp[NT];
     if (tid == 0) pref[a.B] = total;
