@@ -410,13 +410,15 @@ __device__ __forceinline__ const uint8_t* k_src(const AttnArgs& a, int g, const 
 // as inline asm so that the compiler's wait-count bookkeeping does not treat
 // every later LDS read as dependent on it (it would wait for all
 // vector-memory operations, including the next block's V loads); the one
-// reader, the QK of the next block, waits for it explicitly.
+// reader, the QK of the next block, waits for it explicitly. (s_nop 0: one
+// wait state between a scalar write of M0 and the load that uses it, which
+// the compiler pads in its own code but not inside inline asm.)
 template <int S>
 __device__ __forceinline__ void dma_k_group(const uint8_t* src, uint8_t* kw, int c) {
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)kw));
   const uint8_t* gp = src + (int64_t)c * S * 16;
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(lds0 + c * 1024), "v"(gp) : "memory");
 }
 

@@ -390,7 +390,8 @@ void latent_partial_kernel(LatArgs a) {
       const uint32_t s_hi = __builtin_amdgcn_readfirstlane((uint32_t)(s64 >> 32));
       const uint8_t* srcu = (const uint8_t*)(uintptr_t)(((uint64_t)s_hi << 32) | s_lo);
       // recomputed here (opaque to the compiler, three VALU instructions)
-      // rather than kept live across the page and spilled
+      // rather than kept live across the page and spilled; s_nop 0 below:
+      // one wait state between a scalar write of M0 and the copy using it
       uint32_t lane16;
       asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0\n\t"
                    "v_lshlrev_b32 %0, 4, %0" : "=v"(lane16));
@@ -398,7 +399,7 @@ void latent_partial_kernel(LatArgs a) {
       for (int ii = 0; ii < (kWaveChunks + NW - 1) / NW; ++ii) {
         const int i = ii * NW + wv;
         if (kWaveChunks % NW != 0 && i >= kWaveChunks) break;   // uniform
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                      :: "s"(l0 + (uint32_t)i * 1024u), "v"(lane16), "s"(srcu + (int64_t)i * 1024)
                      : "memory");
       }
@@ -413,7 +414,7 @@ void latent_partial_kernel(LatArgs a) {
         uint32_t lane4;
         asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0\n\t"
                      "v_lshlrev_b32 %0, 2, %0" : "=v"(lane4));
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                      :: "s"(ls), "v"(lane4), "s"(tsu) : "memory");
       }
     };

@@ -247,7 +247,8 @@ __global__ __launch_bounds__(64 * NW) void int4_gemm_mfma_kernel(
   const uint32_t xs_lds = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)xs));
   // copy i of tile t: lane L writes position L & 15 of token 4i + (L >> 4)
-  // of the tile, i.e. chunk ((L & 15) - token) mod 16 of that token
+  // of the tile, i.e. chunk ((L & 15) - token) mod 16 of that token (s_nop 0:
+  // one wait state between a scalar write of M0 and the copy using it)
   auto copy_tile = [&](int gi, int slot, int t) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(64 * NW) void int4_gemm_mfma_kernel(
       const int j = ((lane & 15) - tt) & 15;
       const int tok = min(tok0 + 16 * t + tt, m - 1);
       const uint64_t ga = (uint64_t)(uintptr_t)(x + (int64_t)tok * k + kGroup * gi + 8 * j);
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                    :: "s"(xs_lds + (uint32_t)((slot * TILES + t) * kTileB + i * 1024)), "v"(ga)
                    : "memory");
     }
