@@ -80,7 +80,7 @@ def test_library_pool_drives_the_step(gpu, track):
     ovc = okc.copy()
     ks_t, vs_t = torch.from_numpy(ks).to(dev), torch.from_numpy(vs).to(dev)
     u16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
-    # round 1: requests 0..4; round 2: request 5 into request 2's old pages
+    # first batch: requests 0..4; second batch: request 5 into request 2's old pages
     for seqs in ([0, 1, 2, 3, 4], [5]):
         k = np.concatenate([kv[s][0] for s in seqs])
         v = np.concatenate([kv[s][1] for s in seqs])
