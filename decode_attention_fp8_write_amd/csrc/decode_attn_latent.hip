@@ -451,13 +451,16 @@ void latent_partial_kernel(LatArgs a) {
       // so the weights buffer and the rescale factors may be rewritten
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      // Page j's per-token arrays first, then the next page's copy (the other
-      // buffer's last readers, page j - 1, passed the barrier above). Nothing
-      // after the copy waits on the vector memory counter until the top of
-      // the next page, except the rare rescale: a wait there would wait for
-      // the whole copy and serialise it with this page's products.
+      // Page j's per-token arrays. The next page's copy goes out after this
+      // page's QK products, at the start of the softmax (the other buffer's
+      // last readers, page j - 1, passed the barrier above): issued here,
+      // before the barrier below, the 36 copies held every wave at it (a
+      // page took ~3 % longer). Nothing after the copy waits on the vector
+      // memory counter until the top of the next page, except the rare
+      // rescale: a wait there would wait for the whole copy and serialise it
+      // with this page's products.
       finish(j, pb);
-      if (j + 1 < j1) fetch(pid_next, buf[(j + 1 - j0) & 1]);
+      const int pid_copy = pid_next;   // page j + 1, copied below
       pid_next = j + 2 < j1 ? btc[j + 2] : 0;
       __syncthreads();
 
@@ -509,6 +512,10 @@ void latent_partial_kernel(LatArgs a) {
         });
       }
 
+      // the next page's copies, at the start of the softmax (its vector ALU
+      // work leaves memory issue idle; spread over the QK products they
+      // slowed QK, whose LDS reads the copies' writes then met)
+      if (j + 1 < j1) fetch(pid_copy, buf[(j + 1 - j0) & 1]);
       // ---- softmax of this wave's heads (log2 units, scale folded in) -----
       // st[t] register r holds token 16t + 4g + r of head head0 + n
       float bm = -INFINITY;
@@ -555,6 +562,7 @@ void latent_partial_kernel(LatArgs a) {
         *reinterpret_cast<uint2*>(prow_p + 32 * t) = __builtin_bit_cast(uint2, ph);
       }
       }
+      if (!qk && j + 1 < j1) fetch(pid_copy, buf[(j + 1 - j0) & 1]);
       __syncthreads();
 
       // ---- PV: O^T (this wave's dims x all heads) += V^T P^T ---------------

@@ -77,6 +77,10 @@ CASES = [
     ([700, 64], 32),
     ([2048, 1, 333], 64),
     ([130, 95, 4000, 17, 64, 640], 96),
+    # more pages (501) than workgroups (one per CU): fragments of several
+    # pages, so every page after a fragment's first arrives by the copy
+    # issued during the page before it
+    ([20000, 9000, 3000], 64),
 ]
 
 
