@@ -23,8 +23,8 @@
 // products; a wave's own instruction stream is in order):
 //  * the workgroup copies the page's 36 KB of codes and its 64 scales into
 //    LDS by direct global->LDS copies (double-buffered: the next page's copy
-//    is issued once the page's first barrier is passed and runs while the
-//    current one is computed). Tokens past the end are written as zero codes
+//    is issued after the page's QK products, at the start of its softmax,
+//    and lands while the rest of the page is computed). Tokens past the end are written as zero codes
 //    with weight 0, so they contribute nothing and poisoned bytes are never
 //    read into the arithmetic.
 //  * QK is split by heads: wave w < NH owns query heads [16w, 16w+16). S^T =
