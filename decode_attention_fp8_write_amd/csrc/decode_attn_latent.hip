@@ -418,23 +418,18 @@ void latent_partial_kernel(LatArgs a) {
                      :: "s"(ls), "v"(lane4), "s"(tsu) : "memory");
       }
     };
-    // After the copy of page j has landed: zero the codes of tokens past the
-    // end (they then add nothing, whatever the slot held) and fill the
-    // per-token arrays.
-    auto finish = [&](int j, PageBuf& pb) {
+    // Page j's per-token arrays, by wave 0 (the wave that copied the page's
+    // scales) once its own copies of the page have landed: a = c_t sm_scale
+    // log2(e), b = log2(c_t), inv = 1 / c_t, and a = 0, b = -inf, inv = 0 for
+    // tokens past the end.
+    auto factors = [&](int j, PageBuf& pb) {
       const int valid = min(kS, len - j * kS);   // tokens of this page in use
-      if (valid < kS) {
-        for (int c = tid; c < kPageBytes / 16; c += NT)
-          if ((c % kS) >= valid) *reinterpret_cast<uint4*>(pb.codes + c * 16) = make_uint4(0, 0, 0, 0);
-      }
-      if (tid < kS) {
-        // v_log_f32 is log2
-        const float sc = pb.sraw[tid];
-        const bool live = tid < valid;
-        pb.a[tid] = live ? sc * c0 : 0.0f;
-        pb.b[tid] = live ? __builtin_amdgcn_logf(sc) : -INFINITY;
-        pb.inv[tid] = live ? 1.0f / sc : 0.0f;
-      }
+      // lane i: token i (v_log_f32 is log2)
+      const float sc = pb.sraw[lane];
+      const bool live = lane < valid;
+      pb.a[lane] = live ? sc * c0 : 0.0f;
+      pb.b[lane] = live ? __builtin_amdgcn_logf(sc) : -INFINITY;
+      pb.inv[lane] = live ? 1.0f / sc : 0.0f;
     };
 
     // physical page ids are read one page ahead of their copies, through
@@ -444,25 +439,37 @@ void latent_partial_kernel(LatArgs a) {
     ci32l_t* btc = (ci32l_t*)(uintptr_t)btrow;
     int pid_next = j0 + 1 < j1 ? btc[j0 + 1] : 0;
     fetch(btc[j0], buf[0]);
+    if (wv == 0) {
+      __builtin_amdgcn_s_waitcnt(0);
+      factors(j0, buf[0]);
+    }
     for (int j = j0; j < j1; ++j) {
       PageBuf& pb = buf[(j - j0) & 1];
-      // page j's copy (and every earlier load) complete, then publish; past
-      // this barrier every wave has also finished the PV product of page j-1,
-      // so the weights buffer and the rescale factors may be rewritten
+      // page j's copy (and every earlier load) complete, and its per-token
+      // arrays written; then publish. Past this barrier every wave has also
+      // finished the PV product of page j-1, so the weights buffer and the
+      // rescale factors may be rewritten.
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      // Page j's per-token arrays. The next page's copy goes out after this
-      // page's QK products, at the start of the softmax (the other buffer's
-      // last readers, page j - 1, passed the barrier above): issued here,
-      // before the barrier below, the 36 copies held every wave at it (a
-      // page took ~3 % longer). Nothing after the copy waits on the vector
-      // memory counter until the top of the next page, except the rare
-      // rescale: a wait there would wait for the whole copy and serialise it
-      // with this page's products.
-      finish(j, pb);
+      // Tokens past the end (the last page of a sequence only): their codes
+      // are zeroed once the copy has landed, so they add nothing whatever the
+      // slot held, and a second barrier publishes the zeros.
+      {
+        const int valid = min(kS, len - j * kS);
+        if (valid < kS) {
+          for (int c = tid; c < kPageBytes / 16; c += NT)
+            if ((c % kS) >= valid) *reinterpret_cast<uint4*>(pb.codes + c * 16) = make_uint4(0, 0, 0, 0);
+          __syncthreads();
+        }
+      }
+      // The next page's copy goes out after this page's QK products, at the
+      // start of the softmax (the other buffer's last readers, page j - 1,
+      // passed the barrier above). Nothing after the copy waits on the vector
+      // memory counter until the end of the page, except the rare rescale: a
+      // wait there would wait for the whole copy and serialise it with this
+      // page's products.
       const int pid_copy = pid_next;   // page j + 1, copied below
       pid_next = j + 2 < j1 ? btc[j + 2] : 0;
-      __syncthreads();
 
       if (qk) {
       // ---- QK: S^T (64 tokens x 16 heads) as 4 tiles of 16 x 16 ----------
@@ -626,6 +633,16 @@ void latent_partial_kernel(LatArgs a) {
           });
         });
       }
+      // The next page's per-token arrays, by wave 0 after its own copies
+      // (scales included) have landed: it finishes its PV products ahead of
+      // the waves that share its SIMD, so this work (and the wait) mostly
+      // falls in time the barrier at the top of the next page would idle.
+      // The buffer's last readers, the softmax of page j - 1, are past the
+      // barrier before this page's PV.
+      if (wv == 0 && j + 1 < j1) {
+        __builtin_amdgcn_s_waitcnt(0);
+        factors(j + 1, buf[(j + 1 - j0) & 1]);
+      }
     }
 
     // the last PV results land before the accumulators are read (24 wait
@@ -680,28 +697,55 @@ __global__ __launch_bounds__(256) void latent_combine_kernel(LatArgs a) {
   const int* pref = a.hdr + kHdrL;
   const int w0 = owner_of(pref[s], T, W);
   const int w1 = owner_of(pref[s + 1] - 1, T, W);
-  float M = -INFINITY;
+  // Fragments are taken kC at a time: every load of a chunk is issued before
+  // any of its results is used, so a sequence costs one memory round trip
+  // per chunk (two serial loops over the fragments, the maxima first, took
+  // two round trips per fragment). Chunks merge by a running max; with one
+  // chunk this is exactly the max-then-sum rule.
+  constexpr int kC = 8;
+  float M = -INFINITY, L = 0.0f;
+  float4 x0 = z4, x1 = z4;
   bool nan = false;
-  for (int w = w0; w <= w1; ++w) {
-    const float mw = a.part[((int64_t)(w + s) * a.Hq + hd) * kRow + kDv];
-    nan |= __builtin_isnan(mw);
-    M = fmaxf(M, mw);
+  for (int wb = w0; wb <= w1; wb += kC) {
+    float mw[kC], lw[kC];
+    float4 v0[kC], v1[kC];
+    // past the last fragment the index is clamped to it (no branch, so the
+    // chunk's loads stay together) and the entry is given weight 0 below
+#pragma unroll
+    for (int i = 0; i < kC; ++i) {
+      const float* pw = a.part + ((int64_t)(min(wb + i, w1) + s) * a.Hq + hd) * kRow;
+      mw[i] = pw[kDv];
+      lw[i] = pw[kDv + 1];
+      v0[i] = reinterpret_cast<const float4*>(pw + d0)[0];
+      v1[i] = reinterpret_cast<const float4*>(pw + d0)[1];
+    }
+    // (left to itself the compiler issues the rows' loads after the maxima
+    // have arrived: two round trips a chunk)
+    __builtin_amdgcn_sched_barrier(0);
+    float Mc = M;
+#pragma unroll
+    for (int i = 0; i < kC; ++i) {
+      nan |= __builtin_isnan(mw[i]);
+      Mc = fmaxf(Mc, wb + i <= w1 ? mw[i] : -INFINITY);
+    }
+    // what earlier chunks summed under M, rescaled to Mc
+    const float r = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mc);
+    L *= r;
+    x0.x *= r; x0.y *= r; x0.z *= r; x0.w *= r;
+    x1.x *= r; x1.y *= r; x1.z *= r; x1.w *= r;
+#pragma unroll
+    for (int i = 0; i < kC; ++i) {
+      const float f = wb + i <= w1 ? __builtin_amdgcn_exp2f(mw[i] - Mc) : 0.0f;
+      L += f * lw[i];
+      x0.x += f * v0[i].x; x0.y += f * v0[i].y; x0.z += f * v0[i].z; x0.w += f * v0[i].w;
+      x1.x += f * v1[i].x; x1.y += f * v1[i].y; x1.z += f * v1[i].z; x1.w += f * v1[i].w;
+    }
+    M = Mc;
   }
   if (nan) {
     reinterpret_cast<float4*>(o)[0] = n4;
     reinterpret_cast<float4*>(o)[1] = n4;
     return;
-  }
-  float L = 0.0f;
-  float4 x0 = z4, x1 = z4;
-  for (int w = w0; w <= w1; ++w) {
-    const float* pw = a.part + ((int64_t)(w + s) * a.Hq + hd) * kRow;
-    const float f = __builtin_amdgcn_exp2f(pw[kDv] - M);
-    L += f * pw[kDv + 1];
-    const float4 v0 = reinterpret_cast<const float4*>(pw + d0)[0];
-    const float4 v1 = reinterpret_cast<const float4*>(pw + d0)[1];
-    x0.x += f * v0.x; x0.y += f * v0.y; x0.z += f * v0.z; x0.w += f * v0.w;
-    x1.x += f * v1.x; x1.y += f * v1.y; x1.z += f * v1.z; x1.w += f * v1.w;
   }
   const float inv = 1.0f / L;
   reinterpret_cast<float4*>(o)[0] = make_float4(x0.x * inv, x0.y * inv, x0.z * inv, x0.w * inv);
