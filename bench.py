@@ -43,6 +43,7 @@ if ROOT not in sys.path:
 METRIC = ("decode-attn KV GB/s (% HBM peak) + seq-steps/s, FP8 vs BF16 KV, 64×8k ctx")
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD specification
 MFMA_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 / f16 matrix peak, AMD specification
+LATENT_SETTLE_CALLS = 120       # untimed latent calls before its passes (clock settling)
 WORKLOAD_ID = 3
 DEFAULT_SCHEDULE = "serial"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_64x8k.txt")
@@ -385,13 +386,21 @@ def latent_leg(args, torch, synth, pda, workload):
     heads, one 576-dim kv head, per-token scales) on the matrix-core path:
     the attention call timed like the metric's (median of interleaved
     passes of exactly K calls), rated against the dense bf16/f16 matrix
-    peak."""
+    peak. After the shared warm-up the leg makes LATENT_SETTLE_CALLS more
+    untimed calls: under a kernel trace the partial kernel's time rises from
+    ~320 to ~400 us a few calls after the memory-bound legs and settles at
+    285-300 us after about 100 calls (the matrix-heavy kernel follows the
+    chip's clock state; memory-bound kernels move 1-2 %), and the passes
+    are meant to time the settled state a serving loop runs in."""
     batch = synth.make_batch(4)
     log("latent workload: generating inputs and cache")
     db = workload.build(batch, pda.KV_FP8_E4M3, data=gen_data(batch, synth))
     db.alloc_workspace()
     for _ in range(args.warmup):
         db.step()
+    for _ in range(LATENT_SETTLE_CALLS):
+        db.attend()
+    torch.cuda.synchronize()
     t = interleaved_passes({"attn": lambda: db.attend()}, args.steps, args.passes, torch)
     attn_ms = median(t["attn"])
     flops = workload.attention_flops(batch)
@@ -400,6 +409,7 @@ def latent_leg(args, torch, synth, pda, workload):
     log(f"latent attention call: {attn_ms:.4f} ms, {tf:.0f} TFLOP/s")
     out = {"workload": batch.cfg.name, "tokens": int(batch.seq_lens.sum()),
            "attn_ms": attn_ms, "attn_ms_passes": t["attn"],
+           "untimed_calls_before_passes": args.warmup + LATENT_SETTLE_CALLS,
            "roofline": {"kernel": "paged_decode_attn latent (partial + combine)",
                         "bound": "mfma", "achieved": tf, "peak": MFMA_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": tf / MFMA_PEAK_TFLOPS,
