@@ -24,9 +24,12 @@
 //  * the workgroup copies the page's 36 KB of codes and its 64 scales into
 //    LDS by direct global->LDS copies (double-buffered: the next page's copy
 //    is issued after the page's QK products, at the start of its softmax,
-//    and lands while the rest of the page is computed). Tokens past the end are written as zero codes
-//    with weight 0, so they contribute nothing and poisoned bytes are never
-//    read into the arithmetic.
+//    and lands while the rest of the page is computed). Wave 0, which copies
+//    the scales, fills the next page's per-token factors at the end of the
+//    page, so a page takes one barrier before QK and one between softmax and
+//    PV. Tokens past the end are written as zero codes with weight 0 (a
+//    sequence's last page, behind one more barrier), so they contribute
+//    nothing and poisoned bytes are never read into the arithmetic.
 //  * QK is split by heads: wave w < NH owns query heads [16w, 16w+16). S^T =
 //    K Q^T on v_mfma_f32_16x16x32_bf16: K codes convert exactly to bf16 (A
 //    operand, lane = token row, token tile t = tokens 16t .. 16t+15), Q is
