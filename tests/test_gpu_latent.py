@@ -4,7 +4,8 @@ pages of 64 tokens; the MFMA kernel) against the oracle, on small seeded
 problems spanning several pages, ragged last pages and several workgroup
 ranges of the flat page split, plus aborted sequences, the no-op tracker,
 a physical page permutation (bit-identical), poisoned slots (NaN codes and
-NaN scales in every slot no sequence owns) and empty / malformed rows.
+NaN scales in every slot no sequence owns), empty / malformed rows and
+eight seeded random shapes.
 
 Tolerance: max-abs 2e-3 and rel-L2 1e-3 against the fp64 oracle.
 """
@@ -97,6 +98,32 @@ def test_latent_parity(gpu, case):
     assert np.array_equal(g.ts.cpu().numpy().view(np.uint32), ts.view(np.uint32))
     got = g.attend()
     mx, rel = assert_attn_close(got, ref, f"latent case {case}")
+    log(f"  max_abs {mx:.3e} rel_l2 {rel:.3e}")
+    assert np.array_equal(got, g.attend()), "not deterministic"
+
+
+def _random_case(i):
+    """Seeded random latent problem i: 1-12 sequences of 1-3999 tokens, one
+    of them 8000-19999 tokens in about a third of the cases (a sequence over
+    many workgroups' fragments, merged in several chunks), 32-128 heads."""
+    rng = np.random.default_rng(9000 + i)
+    B = int(rng.integers(1, 13))
+    lens = [int(x) for x in rng.integers(1, 4000, B)]
+    if rng.random() < 0.35:
+        lens[int(rng.integers(0, B))] = int(rng.integers(8000, 20000))
+    return lens, int(rng.choice([32, 64, 96, 128])), int(rng.integers(0, 1 << 30))
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_latent_random_shapes(gpu, i):
+    lens, hq, seed = _random_case(i)
+    log(f"latent random case {i}: seed {seed} hq {hq} lens {lens}")
+    pr = small_problem(seed, lens, hq, 1, DK, DV, S, synth.KV_FP8, latent=True)
+    kc, vc, ts = oracle_caches(pr)
+    ref = oracle_attn(pr, kc, vc, ts)
+    g = LatentProblem(gpu, pr)
+    got = g.attend()
+    mx, rel = assert_attn_close(got, ref, f"latent random case {i}")
     log(f"  max_abs {mx:.3e} rel_l2 {rel:.3e}")
     assert np.array_equal(got, g.attend()), "not deterministic"
 
