@@ -1,6 +1,7 @@
 """GPU parity of paged_decode_attn (VALU path, GQA groups below 16 rows)
 against the oracle, on small seeded problems that span several 64-token
-blocks, several split-K chunks and ragged tails, plus the method's edge
+blocks, several split-K chunks and ragged tails (fixed shapes and eight
+seeded random ones over G, kv heads, page size and split), plus the method's edge
 cases: aborted sequences (verdict != 0) read nothing and return zeros, the
 no-op tracker (verdict NULL) matches an all-clear verdict bit for bit, a
 physical page permutation leaves the output bit-identical, poisoned pages
@@ -111,6 +112,38 @@ def test_small_parity(gpu, case, kv_dtype):
     got = g.attend(split=split)
     assert_attn_close(got, ref, f"case {case}")
     # deterministic: a second run is bit-identical
+    assert np.array_equal(got, g.attend(split=split))
+
+
+def _random_case(i):
+    """Seeded random shape i for the vector-ALU path: G in {1, 2, 4, 8},
+    1-8 kv heads, pages of 16, 32 or 64 tokens, split chunks of 0 (automatic)
+    or 64-1024 tokens, 1-10 sequences of 1-2999 tokens (one of 3000-9999 in
+    about a third of the cases)."""
+    rng = np.random.default_rng(7000 + i)
+    G = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    S = int(rng.choice([16, 32, 64]))
+    split = int(rng.choice([0, 64, 128, 192, 512, 1024]))
+    B = int(rng.integers(1, 11))
+    lens = [int(x) for x in rng.integers(1, 3000, B)]
+    if rng.random() < 0.35:
+        lens[int(rng.integers(0, B))] = int(rng.integers(3000, 10000))
+    return lens, G * hkv, hkv, S, split, int(rng.integers(0, 1 << 30))
+
+
+@pytest.mark.parametrize("kv_dtype", [synth.KV_FP8, synth.KV_BF16])
+@pytest.mark.parametrize("i", range(8))
+def test_random_shapes(gpu, i, kv_dtype):
+    lens, hq, hkv, S, split, seed = _random_case(i)
+    log(f"attn random case {i} dtype {kv_dtype}: seed {seed} lens {lens} hq {hq} hkv {hkv} "
+        f"S {S} split {split}")
+    pr = small_problem(seed, lens, hq, hkv, 128, 128, S, kv_dtype)
+    kc, vc, ts = oracle_caches(pr)
+    ref = oracle_attn(pr, kc, vc, ts)
+    g = GpuProblem(gpu, pr)
+    got = g.attend(split=split)
+    assert_attn_close(got, ref, f"random case {i}")
     assert np.array_equal(got, g.attend(split=split))
 
 
